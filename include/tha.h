@@ -1,0 +1,168 @@
+/*
+ * tha.h -- C ABI of libtha.so: one MI355X's share of multi-head scaled
+ * dot-product attention under sequence and head parallelism.
+ *
+ * What the calls compute (pages, by title and section):
+ *  - attention per head: out = softmax(Q K^T * scale + mask) V, with
+ *    scale = 1/sqrt(head_dim) by default ("Megatron-LM - Training
+ *    Multi-Billion Parameter Language Models Using Model Parallelism", the
+ *    linear-algebra-of-attention section; "adv07: Sequence Parallel", Q4;
+ *    "parallel multi-head attention", section 3.2);
+ *  - the Ulysses local layout: sequence shards -> one head group over the
+ *    whole sequence ("adv07: Sequence Parallel", section 5, DeepSpeed Ulysses;
+ *    the all-to-all described as a transpose in the issue thread
+ *    "关于数据分割和合并" of long-context-attention);
+ *  - the Ring local step: attention of one Q chunk against one KV chunk at
+ *    global positions, blocks accumulated into the full result ("adv07:
+ *    Sequence Parallel", Q5 and section 5, Ring Attention).
+ *
+ * Conventions shared by every call:
+ *  - Tensors are contiguous, row-major [batch, seq, heads, head_dim]
+ *    ("parallel multi-head attention" section 3.2; the [b, s/p, n, h] input
+ *    of "Support deepspeed sequence parallel"), head_dim fastest.
+ *    Per-row log-sum-exp tensors are [batch, heads, seq] float32.
+ *  - Every tensor pointer is a DEVICE pointer on the current HIP device.
+ *    Arrays of pointers (o_parts, lse_parts, shards) are HOST arrays holding
+ *    device pointers; the library copies them into kernel arguments, so the
+ *    host arrays may be freed as soon as the call returns.
+ *  - The caller allocates and owns every buffer.  The library allocates no
+ *    memory and keeps no state between calls; calls are safe from several
+ *    host threads.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    default stream).  Outputs are valid once the stream has reached the call.
+ *  - Return value: THA_OK, or a negative tha_status.  Argument errors are
+ *    detected on the host before anything is enqueued (no HIP call is made).
+ *    THA_ERR_HIP means a launch failed; faults inside a kernel surface at the
+ *    caller's next synchronisation, as for any HIP kernel.
+ *  - Outputs must not overlap inputs unless a call says otherwise.
+ */
+#ifndef THA_H
+#define THA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define THA_API __attribute__((visibility("default")))
+
+typedef enum {
+  THA_OK = 0,
+  THA_ERR_INVALID = -1,     /* null pointer, non-positive size, inconsistent sizes */
+  THA_ERR_UNSUPPORTED = -2, /* a valid request this build does not implement */
+  THA_ERR_HIP = -3          /* a HIP launch failed */
+} tha_status;
+
+/* Element types. */
+enum { THA_F32 = 0, THA_BF16 = 1 };
+
+/* attn_fwd mask flags (combinable). */
+enum {
+  THA_MASK_NONE = 0,
+  THA_MASK_CAUSAL = 1,     /* key visible iff k_pos0 + j <= q_pos0 + i ("adv07: Sequence Parallel", Q4) */
+  THA_MASK_KEY_PADDING = 2 /* key j of sequence b visible iff j < kv_len[b] ("Support deepspeed
+                              sequence parallel": the mask is 'token is not padding') */
+};
+
+/* Largest pointer arrays accepted by attn_merge_lse and the permutes. */
+#define THA_MAX_PARTS 64
+#define THA_MAX_SHARDS 64
+
+/*
+ * attn_fwd -- attention of every query row against the visible keys, per head.
+ *
+ *   q      [B, Sq, H, D] of in_dt         k, v   [B, Sk, H, D] of in_dt
+ *   o      [B, Sq, H, D] of out_dt        lse    [B, H, Sq] float32, or NULL
+ *
+ * For batch b, head h and query row i, with s_j = scale * (q_i . k_j) over the
+ * visible keys j:  o_i = sum_j softmax(s)_j v_j,  lse_i = log(sum_j exp(s_j))
+ * (natural log).  Masked keys get weight exactly 0.  A row with no visible key
+ * gets o_i = 0 and lse_i = -inf, so that partial results over disjoint key
+ * blocks can be combined with attn_merge_lse.
+ *
+ * mask_flags: THA_MASK_CAUSAL and/or THA_MASK_KEY_PADDING.  q_pos0 / k_pos0 are
+ * the global sequence positions of query row 0 and key 0 (global position ids,
+ * as in the data collator of "Support deepspeed sequence parallel"); they only
+ * matter with THA_MASK_CAUSAL.  kv_len: device int32 [B], required iff
+ * THA_MASK_KEY_PADDING (values are clamped to [0, Sk] on the device).
+ * scale: multiplies q.k; pass 1/sqrt(D) for standard attention.
+ *
+ * Supported: in_dt = THA_BF16 with D = 64 or 128 (matrix-core path: bf16
+ * products, fp32 accumulation and softmax, probabilities rounded to bf16 before
+ * the product with V, as the forward pass of "parallel multi-head attention"
+ * section 3.2 casts the fp32 softmax back to the input type);
+ * in_dt = THA_F32 with 1 <= D <= 256 (fp32 throughout).  out_dt may be THA_BF16
+ * or THA_F32 in both cases (fp32 output keeps ring partials unrounded).
+ * Errors: THA_ERR_INVALID for null q/k/v/o, non-positive sizes, unknown mask
+ * bits, KEY_PADDING without kv_len, non-finite scale, |q_pos0| or |k_pos0| >=
+ * 2^62; THA_ERR_UNSUPPORTED for other dtypes / head dims.
+ */
+THA_API int attn_fwd(const void* q, const void* k, const void* v, void* o, int out_dt, float* lse, int B, int Sq,
+             int Sk, int H, int D, int in_dt, unsigned mask_flags, long long q_pos0, long long k_pos0,
+             const int* kv_len, float scale, void* stream);
+
+/*
+ * attn_merge_lse -- combine n partial attention results over disjoint key
+ * sets into the result over their union (the Ring step "accumulate block
+ * results into the full attention", "adv07: Sequence Parallel" Q5; the
+ * combination rule itself is the standard log-sum-exp one, a reading):
+ *   M = max_k lse_k;  w_k = exp(lse_k - M);  o = sum_k w_k o_k / sum_k w_k;
+ *   lse = M + log(sum_k w_k);  rows where every lse_k = -inf give o = 0,
+ *   lse = -inf.
+ *
+ *   o_parts   host array of n_parts device pointers, each [B, S, H, D] of part_dt
+ *   lse_parts host array of n_parts device pointers, each [B, H, S] float32
+ *   o_out     [B, S, H, D] of out_dt; may alias o_parts[0] when part_dt == out_dt
+ *   lse_out   [B, H, S] float32 or NULL; may alias lse_parts[0]
+ * 1 <= n_parts <= THA_MAX_PARTS; part_dt, out_dt in {THA_F32, THA_BF16}.
+ * Errors: THA_ERR_INVALID for null pointers, n_parts out of range,
+ * non-positive sizes, or o_out aliasing o_parts[0] with differing dtypes;
+ * THA_ERR_UNSUPPORTED for other dtypes.
+ */
+THA_API int attn_merge_lse(int n_parts, const void* const* o_parts, const float* const* lse_parts, int part_dt,
+                   void* o_out, int out_dt, float* lse_out, int B, int S, int H, int D, void* stream);
+
+/*
+ * shard_permute -- the local layout effect of the Ulysses all-to-all that
+ * gathers the sequence and scatters heads ("adv07: Sequence Parallel" section
+ * 5, DeepSpeed Ulysses: each device computes its heads over all positions;
+ * the issue thread "关于数据分割和合并" calls it a transpose).  Shard i holds
+ * tokens [i*S/P, (i+1)*S/P) with all H heads (the per-rank slices of the data
+ * collator in "Support deepspeed sequence parallel"); head group g is heads
+ * [g*H/P, (g+1)*H/P) (whole heads per device, "parallel multi-head attention"
+ * sections 2.2 and 3.1).
+ *
+ *   shards  host array of P device pointers, each [B, S/P, H, D]
+ *   out     [B, S, H/P, D]:  out[b, i*S/P + t, hh, d] = shard_i[b, t, g*H/P + hh, d]
+ * elem_bytes in {1, 2, 4, 8}; bytes are copied verbatim (bit-exact).
+ * Errors: THA_ERR_INVALID for null pointers, P outside [1, THA_MAX_SHARDS],
+ * group outside [0, P), S or H not divisible by P, non-positive sizes;
+ * THA_ERR_UNSUPPORTED for other elem_bytes.
+ */
+THA_API int shard_permute(const void* const* shards, int P, int group, void* out, int B, int S, int H, int D,
+                  int elem_bytes, void* stream);
+
+/*
+ * shard_unpermute -- the inverse layout (the all-to-all that returns each
+ * device's heads to sequence shards after attention, issue thread
+ * "关于数据分割和合并": outputs stay sequence-sharded, (bs, seqlen/N, hidden)).
+ *
+ *   in      [B, S, H/P, D], head group `group` over the whole sequence
+ *   shards  host array of P device pointers, each [B, S/P, H, D]; only the
+ *           heads of `group` are written:
+ *           shard_i[b, t, g*H/P + hh, d] = in[b, i*S/P + t, hh, d]
+ * Same argument rules and errors as shard_permute.
+ */
+THA_API int shard_unpermute(const void* in, int P, int group, void* const* shards, int B, int S, int H, int D,
+                    int elem_bytes, void* stream);
+
+/* Static description of a status code (never NULL). */
+THA_API const char* tha_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+THA_API int tha_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* THA_H */

@@ -1,0 +1,177 @@
+"""Python binding of libtha.so (the C ABI declared in include/tha.h).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the computation runs in the library's HIP kernels.
+There is no fallback: if libtha.so is missing or fails to load, every call
+raises.  Build it with `python -m tensor_head_attention_amd.build`.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtha.so")
+
+THA_OK, THA_ERR_INVALID, THA_ERR_UNSUPPORTED, THA_ERR_HIP = 0, -1, -2, -3
+THA_F32, THA_BF16 = 0, 1
+THA_MASK_NONE, THA_MASK_CAUSAL, THA_MASK_KEY_PADDING = 0, 1, 2
+THA_MAX_PARTS = THA_MAX_SHARDS = 64
+
+_lib = None
+
+
+class ThaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status) if _lib is not None else status} (status {status})")
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libtha.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build it with `python -m tensor_head_attention_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, ci, cll = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, ci, vp, ci, ci, ci, ci, ci, ci, ctypes.c_uint, cll, cll, vp,
+                             ctypes.c_float, vp]
+    lib.attn_merge_lse.argtypes = [ci, vp, vp, ci, vp, ci, vp, ci, ci, ci, ci, vp]
+    lib.shard_permute.argtypes = [vp, ci, ci, vp, ci, ci, ci, ci, ci, vp]
+    lib.shard_unpermute.argtypes = [vp, ci, ci, vp, ci, ci, ci, ci, ci, vp]
+    for f in (lib.attn_fwd, lib.attn_merge_lse, lib.shard_permute, lib.shard_unpermute, lib.tha_version):
+        f.restype = ci
+    lib.tha_status_string.argtypes = [ci]
+    lib.tha_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().tha_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return load_library().tha_version()
+
+
+def _check(rc: int, what: str):
+    if rc == THA_OK:
+        return
+    if rc == THA_ERR_INVALID:
+        raise ValueError(f"{what}: {status_string(rc)}")
+    if rc == THA_ERR_UNSUPPORTED:
+        raise NotImplementedError(f"{what}: {status_string(rc)}")
+    raise ThaError(rc, what)
+
+
+def _dt(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return THA_BF16
+    if t == torch.float32:
+        return THA_F32
+    raise NotImplementedError(f"unsupported dtype {t}")
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptrs(ts: Sequence[torch.Tensor]):
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+             kv_len: Optional[torch.Tensor] = None, q_pos0: int = 0, k_pos0: int = 0,
+             scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
+             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+             return_lse: bool = True):
+    """out [B,Sq,H,D], lse [B,H,Sq] (fp32) = attention of q against k/v (see tha.h attn_fwd)."""
+    load_library()
+    q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    if out is None:
+        out = torch.empty((B, Sq, H, D), dtype=out_dtype or q.dtype, device=q.device)
+    _dev(out, "out")
+    if lse is None and return_lse:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    flags = THA_MASK_CAUSAL if causal else 0
+    kvp = None
+    if kv_len is not None:
+        kv_len = _dev(kv_len, "kv_len")
+        if kv_len.dtype != torch.int32:
+            raise ValueError("kv_len must be int32")
+        flags |= THA_MASK_KEY_PADDING
+        kvp = kv_len.data_ptr()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rc = _lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dt(out.dtype),
+                       lse.data_ptr() if lse is not None else None, B, Sq, Sk, H, D, _dt(q.dtype), flags,
+                       int(q_pos0), int(k_pos0), kvp, float(scale), _stream(q))
+    _check(rc, "attn_fwd")
+    return (out, lse) if return_lse else out
+
+
+def attn_merge_lse(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Tensor], *,
+                   out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                   lse_out: Optional[torch.Tensor] = None, return_lse: bool = True):
+    """Log-sum-exp merge of partial results (see tha.h attn_merge_lse)."""
+    load_library()
+    if len(o_parts) != len(lse_parts) or len(o_parts) == 0:
+        raise ValueError("need matching, non-empty o_parts and lse_parts")
+    for i, (o, l) in enumerate(zip(o_parts, lse_parts)):
+        _dev(o, f"o_parts[{i}]"), _dev(l, f"lse_parts[{i}]")
+        if l.dtype != torch.float32:
+            raise ValueError("lse parts must be float32")
+    B, S, H, D = o_parts[0].shape
+    part_dt = _dt(o_parts[0].dtype)
+    if out is None:
+        out = torch.empty((B, S, H, D), dtype=out_dtype or o_parts[0].dtype, device=o_parts[0].device)
+    if lse_out is None and return_lse:
+        lse_out = torch.empty((B, H, S), dtype=torch.float32, device=o_parts[0].device)
+    rc = _lib.attn_merge_lse(len(o_parts), _ptrs(o_parts), _ptrs(lse_parts), part_dt, out.data_ptr(),
+                             _dt(out.dtype), lse_out.data_ptr() if lse_out is not None else None, B, S, H, D,
+                             _stream(out))
+    _check(rc, "attn_merge_lse")
+    return (out, lse_out) if return_lse else out
+
+
+def shard_permute(shards: Sequence[torch.Tensor], group: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """P sequence shards [B,S/P,H,D] -> head group `group` over the whole sequence [B,S,H/P,D]."""
+    load_library()
+    shards = [_dev(s, f"shards[{i}]") for i, s in enumerate(shards)]
+    P = len(shards)
+    B, Sl, H, D = shards[0].shape
+    if out is None:
+        out = torch.empty((B, Sl * P, H // P if P else H, D), dtype=shards[0].dtype, device=shards[0].device)
+    rc = _lib.shard_permute(_ptrs(shards), P, int(group), _dev(out, "out").data_ptr(), B, Sl * P, H, D,
+                            shards[0].element_size(), _stream(out))
+    _check(rc, "shard_permute")
+    return out
+
+
+def shard_unpermute(x: torch.Tensor, group: int, shards: Sequence[torch.Tensor]) -> None:
+    """Write head group `group` of x [B,S,H/P,D] back into the P sequence shards [B,S/P,H,D]."""
+    load_library()
+    x = _dev(x, "x")
+    shards = [_dev(s, f"shards[{i}]") for i, s in enumerate(shards)]
+    P = len(shards)
+    B, S, Hl, D = x.shape
+    rc = _lib.shard_unpermute(x.data_ptr(), P, int(group), _ptrs(shards), B, S, Hl * P, D, x.element_size(),
+                              _stream(x))
+    _check(rc, "shard_unpermute")

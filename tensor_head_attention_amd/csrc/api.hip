@@ -1,0 +1,110 @@
+// api.hip -- the C ABI of libtha.so (declared in include/tha.h): argument
+// validation on the host, then dispatch to the kernel launchers.  Validation
+// runs before any HIP call, so every argument error is reported without
+// touching a device.
+#include <math.h>
+#include <stdint.h>
+
+#include "tha.h"
+#include "tha_kernels.h"
+
+namespace {
+
+constexpr long long kMaxPos = 1LL << 62;
+constexpr int64_t kMaxRowElems = 1LL << 24;  // H*D per token: tile offsets stay 32-bit
+
+int hip_status(hipError_t e) { return e == hipSuccess ? THA_OK : THA_ERR_HIP; }
+
+bool dtype_ok(int dt) { return dt == THA_F32 || dt == THA_BF16; }
+
+int check_permute(const void* grouped, const void* const* shards, int P, int group, int B, int S, int H, int D,
+                  int elem_bytes) {
+  if (!grouped || !shards) return THA_ERR_INVALID;
+  if (P < 1 || P > THA_MAX_SHARDS) return THA_ERR_INVALID;
+  if (group < 0 || group >= P) return THA_ERR_INVALID;
+  if (B <= 0 || S <= 0 || H <= 0 || D <= 0) return THA_ERR_INVALID;
+  if (S % P != 0 || H % P != 0) return THA_ERR_INVALID;
+  for (int i = 0; i < P; ++i)
+    if (!shards[i]) return THA_ERR_INVALID;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) return THA_ERR_UNSUPPORTED;
+  if ((int64_t)H * D > kMaxRowElems) return THA_ERR_UNSUPPORTED;
+  return THA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tha_version(void) { return 100; }
+
+const char* tha_status_string(int status) {
+  switch (status) {
+    case THA_OK: return "ok";
+    case THA_ERR_INVALID: return "invalid argument";
+    case THA_ERR_UNSUPPORTED: return "unsupported dtype, head dim or size";
+    case THA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, int out_dt, float* lse, int B, int Sq, int Sk,
+             int H, int D, int in_dt, unsigned mask_flags, long long q_pos0, long long k_pos0, const int* kv_len,
+             float scale, void* stream) {
+  if (!q || !k || !v || !o) return THA_ERR_INVALID;
+  if (B <= 0 || Sq <= 0 || Sk <= 0 || H <= 0 || D <= 0) return THA_ERR_INVALID;
+  if (mask_flags & ~(unsigned)(THA_MASK_CAUSAL | THA_MASK_KEY_PADDING)) return THA_ERR_INVALID;
+  if ((mask_flags & THA_MASK_KEY_PADDING) && !kv_len) return THA_ERR_INVALID;
+  if (!isfinite(scale)) return THA_ERR_INVALID;
+  if (q_pos0 >= kMaxPos || q_pos0 <= -kMaxPos || k_pos0 >= kMaxPos || k_pos0 <= -kMaxPos) return THA_ERR_INVALID;
+  if (!dtype_ok(in_dt) || !dtype_ok(out_dt)) return THA_ERR_UNSUPPORTED;
+  if ((int64_t)H * D > kMaxRowElems) return THA_ERR_UNSUPPORTED;
+  if (in_dt == THA_BF16 && D != 128 && D != 64) return THA_ERR_UNSUPPORTED;
+  if (in_dt == THA_F32 && D > 256) return THA_ERR_UNSUPPORTED;
+  tha::AttnArgs a;
+  a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse;
+  a.kv_len = (mask_flags & THA_MASK_KEY_PADDING) ? kv_len : nullptr;
+  a.B = B, a.Sq = Sq, a.Sk = Sk, a.H = H, a.D = D;
+  a.out_dt = out_dt;
+  a.causal = (mask_flags & THA_MASK_CAUSAL) != 0;
+  a.q_pos0 = q_pos0, a.k_pos0 = k_pos0;
+  a.scale = scale;
+  hipStream_t st = (hipStream_t)stream;
+  return hip_status(in_dt == THA_BF16 ? tha::launch_attn_bf16(a, st) : tha::launch_attn_f32(a, st));
+}
+
+int attn_merge_lse(int n_parts, const void* const* o_parts, const float* const* lse_parts, int part_dt, void* o_out,
+                   int out_dt, float* lse_out, int B, int S, int H, int D, void* stream) {
+  if (n_parts < 1 || n_parts > THA_MAX_PARTS) return THA_ERR_INVALID;
+  if (!o_parts || !lse_parts || !o_out) return THA_ERR_INVALID;
+  if (B <= 0 || S <= 0 || H <= 0 || D <= 0) return THA_ERR_INVALID;
+  tha::PartPtrs pp = {};
+  for (int i = 0; i < n_parts; ++i) {
+    if (!o_parts[i] || !lse_parts[i]) return THA_ERR_INVALID;
+    pp.o[i] = o_parts[i];
+    pp.lse[i] = lse_parts[i];
+  }
+  if (!dtype_ok(part_dt) || !dtype_ok(out_dt)) return THA_ERR_UNSUPPORTED;
+  if (o_out == o_parts[0] && part_dt != out_dt) return THA_ERR_INVALID;
+  return hip_status(
+      tha::launch_merge_lse(n_parts, pp, part_dt, o_out, out_dt, lse_out, B, S, H, D, (hipStream_t)stream));
+}
+
+int shard_permute(const void* const* shards, int P, int group, void* out, int B, int S, int H, int D, int elem_bytes,
+                  void* stream) {
+  const int rc = check_permute(out, shards, P, group, B, S, H, D, elem_bytes);
+  if (rc != THA_OK) return rc;
+  tha::ShardPtrs sp = {};
+  for (int i = 0; i < P; ++i) sp.p[i] = const_cast<void*>(shards[i]);
+  return hip_status(tha::launch_shard_permute(sp, P, group, out, B, S, H, D, elem_bytes, (hipStream_t)stream));
+}
+
+int shard_unpermute(const void* in, int P, int group, void* const* shards, int B, int S, int H, int D, int elem_bytes,
+                    void* stream) {
+  const int rc = check_permute(in, (const void* const*)shards, P, group, B, S, H, D, elem_bytes);
+  if (rc != THA_OK) return rc;
+  tha::ShardPtrs sp = {};
+  for (int i = 0; i < P; ++i) sp.p[i] = shards[i];
+  return hip_status(tha::launch_shard_unpermute(in, P, group, sp, B, S, H, D, elem_bytes, (hipStream_t)stream));
+}
+
+}  // extern "C"

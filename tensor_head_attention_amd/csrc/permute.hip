@@ -1,0 +1,147 @@
+// permute.hip -- Ulysses local layout kernels: sequence shards <-> one head group
+// over the whole sequence (the local effect of the all-to-all that "adv07:
+// Sequence Parallel", section 5 (DeepSpeed Ulysses) describes, a transpose of
+// the sequence and head axes in the issue thread "关于数据分割和合并").
+//
+// Both directions are a gather/scatter of contiguous runs: for every (b, s)
+// token the head group's heads are R = (H/P)*D*elem_bytes contiguous bytes in
+// the shard (inside a row of H*D elements) and R contiguous bytes in the
+// grouped tensor.  The grouped side is walked linearly so that one side of
+// every copy is a fully contiguous stream; the other side is R-byte runs.
+//
+// HBM-bound: each byte is read once and written once.  16-byte vector path when
+// R and every pointer are 16-byte aligned; element-wise fallback otherwise.
+#include "device_common.h"
+#include "tha_kernels.h"
+
+namespace tha {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kVecPerThread = 4;  // independent 16 B loads in flight per thread
+
+// Vector path.  Thread item index idx (of 16 B) in the grouped tensor [B, S, H/P, D]
+// maps to token (b, s) = idx / run_vecs and vector v = idx % run_vecs.
+template <bool kToGroup>
+__global__ void __launch_bounds__(kThreads) permute_vec_kernel(ShardPtrs shards, char* grouped, int64_t total_vecs,
+                                                              uint32_t run_vecs, uint32_t run_shift, int S, int Sl,
+                                                              int64_t shard_row_bytes, int64_t group_off_bytes) {
+  const int64_t base = ((int64_t)blockIdx.x * kThreads * kVecPerThread) + threadIdx.x;
+  i32x4 buf[kVecPerThread];
+  int64_t gidx[kVecPerThread];
+  const char* src[kVecPerThread];
+  char* dst[kVecPerThread];
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u) {
+    const int64_t idx = base + (int64_t)u * kThreads;
+    gidx[u] = idx;
+    if (idx >= total_vecs) continue;
+    int64_t tok;
+    uint32_t v;
+    if (run_shift != 0xffffffffu) {  // power-of-two run length
+      tok = idx >> run_shift;
+      v = (uint32_t)(idx & (run_vecs - 1));
+    } else {
+      tok = idx / run_vecs;
+      v = (uint32_t)(idx - tok * run_vecs);
+    }
+    const int64_t b = tok / S;
+    const int s = (int)(tok - b * S);
+    const int i = s / Sl;
+    const int t = s - i * Sl;
+    char* shard_p = (char*)shards.p[i] + (b * Sl + t) * shard_row_bytes + group_off_bytes + (int64_t)v * 16;
+    char* group_p = grouped + idx * 16;
+    src[u] = kToGroup ? shard_p : group_p;
+    dst[u] = kToGroup ? group_p : shard_p;
+  }
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u)
+    if (gidx[u] < total_vecs) buf[u] = __builtin_nontemporal_load((const i32x4*)src[u]);
+#pragma unroll
+  for (int u = 0; u < kVecPerThread; ++u)
+    if (gidx[u] < total_vecs) __builtin_nontemporal_store(buf[u], (i32x4*)dst[u]);
+}
+
+// Element-wise fallback for unaligned or odd-sized runs.
+template <typename T, bool kToGroup>
+__global__ void __launch_bounds__(kThreads) permute_elem_kernel(ShardPtrs shards, T* grouped, int64_t total,
+                                                               int64_t run_elems, int S, int Sl,
+                                                               int64_t shard_row_elems, int64_t group_off_elems) {
+  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < total;
+       idx += (int64_t)gridDim.x * kThreads) {
+    const int64_t tok = idx / run_elems;
+    const int64_t e = idx - tok * run_elems;
+    const int64_t b = tok / S;
+    const int s = (int)(tok - b * S);
+    const int i = s / Sl;
+    const int t = s - i * Sl;
+    T* shard_p = (T*)shards.p[i] + (b * Sl + t) * shard_row_elems + group_off_elems + e;
+    if (kToGroup)
+      grouped[idx] = *shard_p;
+    else
+      *shard_p = grouped[idx];
+  }
+}
+
+template <typename T, bool kToGroup>
+hipError_t launch_elem(const ShardPtrs& sp, void* grouped, int64_t total, int64_t run_elems, int S, int Sl,
+                       int64_t row_elems, int64_t off_elems, hipStream_t st) {
+  int64_t blocks = (total + kThreads - 1) / kThreads;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL((permute_elem_kernel<T, kToGroup>), dim3((unsigned)blocks), dim3(kThreads), 0, st, sp,
+                     (T*)grouped, total, run_elems, S, Sl, row_elems, off_elems);
+  return hipGetLastError();
+}
+
+template <bool kToGroup>
+hipError_t launch_permute(const ShardPtrs& sp, int P, int group, void* grouped, int B, int S, int H, int D,
+                          int eb, hipStream_t st) {
+  const int Sl = S / P, Hl = H / P;
+  const int64_t run_bytes = (int64_t)Hl * D * eb;
+  const int64_t row_bytes = (int64_t)H * D * eb;
+  const int64_t off_bytes = (int64_t)group * Hl * D * eb;
+  bool aligned = (run_bytes % 16 == 0) && (row_bytes % 16 == 0) && (off_bytes % 16 == 0) &&
+                 ((uintptr_t)grouped % 16 == 0);
+  for (int i = 0; i < P && aligned; ++i) aligned = ((uintptr_t)sp.p[i] % 16 == 0);
+  const int64_t tokens = (int64_t)B * S;
+  if (aligned && run_bytes / 16 <= 0x7fffffff) {
+    const uint32_t run_vecs = (uint32_t)(run_bytes / 16);
+    uint32_t shift = 0xffffffffu;
+    if ((run_vecs & (run_vecs - 1)) == 0) {
+      shift = 0;
+      while ((1u << shift) < run_vecs) ++shift;
+    }
+    const int64_t total = tokens * run_vecs;
+    const int64_t per_block = (int64_t)kThreads * kVecPerThread;
+    const int64_t blocks = (total + per_block - 1) / per_block;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((permute_vec_kernel<kToGroup>), dim3((unsigned)blocks), dim3(kThreads), 0, st, sp,
+                       (char*)grouped, total, run_vecs, shift, S, Sl, row_bytes, off_bytes);
+    return hipGetLastError();
+  }
+  const int64_t run_elems = (int64_t)Hl * D;
+  const int64_t total = tokens * run_elems;
+  const int64_t row_elems = (int64_t)H * D, off_elems = (int64_t)group * Hl * D;
+  switch (eb) {
+    case 1: return launch_elem<uint8_t, kToGroup>(sp, grouped, total, run_elems, S, Sl, row_elems, off_elems, st);
+    case 2: return launch_elem<uint16_t, kToGroup>(sp, grouped, total, run_elems, S, Sl, row_elems, off_elems, st);
+    case 4: return launch_elem<uint32_t, kToGroup>(sp, grouped, total, run_elems, S, Sl, row_elems, off_elems, st);
+    case 8: return launch_elem<uint64_t, kToGroup>(sp, grouped, total, run_elems, S, Sl, row_elems, off_elems, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_shard_permute(const ShardPtrs& shards, int P, int group, void* out, int B, int S, int H, int D,
+                                int elem_bytes, hipStream_t stream) {
+  return launch_permute<true>(shards, P, group, out, B, S, H, D, elem_bytes, stream);
+}
+
+hipError_t launch_shard_unpermute(const void* in, int P, int group, const ShardPtrs& shards, int B, int S, int H,
+                                  int D, int elem_bytes, hipStream_t stream) {
+  return launch_permute<false>(shards, P, group, const_cast<void*>(in), B, S, H, D, elem_bytes, stream);
+}
+
+}  // namespace tha

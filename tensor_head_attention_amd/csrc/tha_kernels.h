@@ -1,0 +1,43 @@
+// tha_kernels.h -- internal launcher interface between the C ABI (api.hip) and the
+// kernel translation units.  Arguments are validated by the caller.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tha.h"
+
+namespace tha {
+
+// Device pointers passed by value in the kernel argument block.
+struct ShardPtrs {
+  void* p[THA_MAX_SHARDS];
+};
+struct PartPtrs {
+  const void* o[THA_MAX_PARTS];
+  const float* lse[THA_MAX_PARTS];
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int* kv_len;  // nullptr unless key padding
+  int B, Sq, Sk, H, D;
+  int out_dt;
+  bool causal;
+  long long q_pos0, k_pos0;
+  float scale;
+};
+
+hipError_t launch_shard_permute(const ShardPtrs& shards, int P, int group, void* out, int B, int S, int H, int D,
+                                int elem_bytes, hipStream_t stream);
+hipError_t launch_shard_unpermute(const void* in, int P, int group, const ShardPtrs& shards, int B, int S, int H,
+                                  int D, int elem_bytes, hipStream_t stream);
+hipError_t launch_merge_lse(int n_parts, const PartPtrs& parts, int part_dt, void* o_out, int out_dt, float* lse_out,
+                            int B, int S, int H, int D, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
+
+}  // namespace tha

@@ -1,0 +1,128 @@
+"""CPU checks of the C-ABI library: it loads, exports every declared entry point,
+and rejects bad arguments on the host before any HIP call (no device needed)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import tensor_head_attention_amd as T
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        txt = open(h).read()
+        names += re.findall(r"^THA_API\s+[\w\s\*]*?\b(\w+)\s*\(", txt, re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(T.LIB_PATH):
+        import tensor_head_attention_amd.build as b
+        b.build_library()
+    return T.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared_symbols()
+    assert {"attn_fwd", "attn_merge_lse", "shard_permute", "shard_unpermute", "tha_status_string",
+            "tha_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert T.version() >= 100
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, 7):
+        assert isinstance(T.status_string(s), str) and T.status_string(s)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    saved = T._lib
+    try:
+        T._lib = None
+        with pytest.raises(RuntimeError):
+            T.load_library(str(tmp_path / "nope.so"))
+    finally:
+        T._lib = saved
+
+
+P = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails before any HIP call
+
+
+def _attn(lib, q=P, k=P, v=P, o=P, out_dt=1, lse=None, B=1, Sq=8, Sk=8, H=1, D=128, in_dt=1, flags=0, qp=0, kp=0,
+          kv=None, scale=0.088, stream=None):
+    return lib.attn_fwd(q, k, v, o, out_dt, lse, B, Sq, Sk, H, D, in_dt, flags, qp, kp, kv, scale, stream)
+
+
+def test_attn_fwd_validation(lib):
+    E, U = T.THA_ERR_INVALID, T.THA_ERR_UNSUPPORTED
+    assert _attn(lib, q=None) == E
+    assert _attn(lib, k=None) == E
+    assert _attn(lib, v=None) == E
+    assert _attn(lib, o=None) == E
+    for kw in ("B", "Sq", "Sk", "H", "D"):
+        assert _attn(lib, **{kw: 0}) == E
+        assert _attn(lib, **{kw: -3}) == E
+    assert _attn(lib, flags=4) == E                      # unknown mask bit
+    assert _attn(lib, flags=T.THA_MASK_KEY_PADDING) == E  # key padding without kv_len
+    assert _attn(lib, scale=float("inf")) == E
+    assert _attn(lib, scale=float("nan")) == E
+    assert _attn(lib, qp=1 << 62) == E
+    assert _attn(lib, kp=-(1 << 62)) == E
+    assert _attn(lib, in_dt=5) == U
+    assert _attn(lib, out_dt=9) == U
+    assert _attn(lib, D=96) == U                         # bf16 path: D in {64, 128}
+    assert _attn(lib, in_dt=0, D=257) == U               # fp32 path: D <= 256
+    assert _attn(lib, H=1 << 20, D=128) == U             # token row too long for 32-bit tile offsets
+
+
+def _ptr_arr(n, val=0x1000):
+    return (ctypes.c_void_p * n)(*([val] * n))
+
+
+def test_merge_validation(lib):
+    E, U = T.THA_ERR_INVALID, T.THA_ERR_UNSUPPORTED
+    o, l = _ptr_arr(2), _ptr_arr(2)
+    ok = dict(n=2, o=o, l=l, pdt=0, out=P, odt=1, lo=None, B=1, S=4, H=2, D=8)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.attn_merge_lse(a["n"], a["o"], a["l"], a["pdt"], a["out"], a["odt"], a["lo"], a["B"], a["S"],
+                                  a["H"], a["D"], None)
+    assert call(n=0) == E
+    assert call(n=65) == E
+    assert call(o=None) == E
+    assert call(l=None) == E
+    assert call(out=None) == E
+    assert call(o=(ctypes.c_void_p * 2)(0x1000, 0)) == E
+    assert call(S=0) == E
+    assert call(D=-1) == E
+    assert call(pdt=3) == U
+    assert call(odt=3) == U
+    assert call(o=_ptr_arr(2, 0x2000), out=ctypes.c_void_p(0x2000), pdt=0, odt=1) == E  # in place, dtypes differ
+
+
+def test_permute_validation(lib):
+    E, U = T.THA_ERR_INVALID, T.THA_ERR_UNSUPPORTED
+    sh = _ptr_arr(4)
+    for fn in (lambda *a: lib.shard_permute(a[0], a[1], a[2], a[3], *a[4:]),
+               lambda *a: lib.shard_unpermute(a[3], a[1], a[2], a[0], *a[4:])):
+        def call(shards=sh, Pn=4, g=0, out=P, B=1, S=8, H=8, D=4, eb=2):
+            return fn(shards, Pn, g, out, B, S, H, D, eb, None)
+        assert call(shards=None) == E
+        assert call(out=None) == E
+        assert call(Pn=0) == E
+        assert call(Pn=65, shards=_ptr_arr(65)) == E
+        assert call(g=4) == E
+        assert call(g=-1) == E
+        assert call(S=10) == E   # S % P
+        assert call(H=6) == E    # H % P
+        assert call(B=0) == E
+        assert call(shards=(ctypes.c_void_p * 4)(0x1000, 0x1000, 0, 0x1000)) == E
+        assert call(eb=3) == U
