@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark: one MI355X's Ulysses share of head/sequence-parallel attention.
+
+A step is one pass of the hot path over one batch of seeded synthetic input:
+three shard_permute calls (Q, K, V: 8 sequence shards [1, 4096, 64, 128] bf16
+-> head group 0 over the whole sequence, [1, 32768, 8, 128]) followed by causal
+attn_fwd over S = 32768 for those 8 heads (head_dim 128, bf16 in, fp32
+accumulate, bf16 out + fp32 LSE).  Inputs are resident in HBM before timing.
+
+value = algorithmic attention FLOP of a step / step time (TFLOP/s), where the
+FLOP count covers only visible (query, key) pairs, 4*D per pair.
+
+Side measurements (not part of `value`): each kernel's own rate, and the Ring
+share (one 4096-row Q chunk at positions 28672.. against 8 KV chunks, fp32
+partials, one 8-way attn_merge_lse).
+
+The CPU baseline times the fp64 oracle on a bounded sample of the same
+attention (a set of query rows, all heads) on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def causal_pairs(Sq: int, Sk: int, q_pos0: int, k_pos0: int) -> int:
+    """Visible (query, key) pairs of one head under the causal rule k_pos0 + j <= q_pos0 + i."""
+    tot = 0
+    # rows whose visible prefix is clipped at Sk contribute Sk; others q_pos0 + i - k_pos0 + 1 (>= 0)
+    for i in range(Sq):
+        n = q_pos0 + i - k_pos0 + 1
+        tot += max(0, min(Sk, n))
+    return tot
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows in the oracle's timed sample")
+    ap.add_argument("--no-side", action="store_true", help="skip the Ring-share side measurement")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU's share only; --gpus must be 1 "
+              "(the multi-GPU exchange is not part of it).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import tensor_head_attention_amd as T
+    import tha_workloads as W
+
+    if not os.path.exists(T.LIB_PATH):
+        from tensor_head_attention_amd import build as hb
+        hb.build_library()
+    T.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    inp, p = W.workload_inputs(3, seed=args.seed)
+    P, S, H, D, grp = p["P"], p["S"], p["H"], p["D"], p["group"]
+    Hl = H // P
+    shards = {n: [t.to(dev) for t in inp[n]] for n in ("q", "k", "v")}
+    del inp
+    grouped = {n: torch.empty((1, S, Hl, D), dtype=torch.bfloat16, device=dev) for n in ("q", "k", "v")}
+    out = torch.empty((1, S, Hl, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((1, Hl, S), dtype=torch.float32, device=dev)
+    flops = 4.0 * D * Hl * causal_pairs(S, S, 0, 0)
+    permute_bytes = 2.0 * S * Hl * D * 2  # group slice read once + grouped tensor written once
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(rec=None):
+        if rec is not None:
+            rec[0].record()
+        for n in ("q", "k", "v"):
+            T.shard_permute(shards[n], grp, out=grouped[n])
+        if rec is not None:
+            rec[1].record()
+        T.attn_fwd(grouped["q"], grouped["k"], grouped["v"], causal=True, out=out, lse=lse)
+        if rec is not None:
+            rec[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    recs = [(ev(), ev(), ev()) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    torch.cuda.synchronize()
+    for r in recs:
+        step(r)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    perm_ms = sum(r[0].elapsed_time(r[1]) for r in recs) / args.steps / 3.0   # one permute call
+    attn_ms = sum(r[1].elapsed_time(r[2]) for r in recs) / args.steps
+    step_ms = sum(r[0].elapsed_time(r[2]) for r in recs) / args.steps
+    step_ms = max(step_ms, wall * 1e3 / args.steps)
+    value = flops / (step_ms * 1e-3) / 1e12
+    attn_tflops = flops / (attn_ms * 1e-3) / 1e12
+
+    components = {
+        "shard_permute": {"us_per_call": perm_ms * 1e3, "bytes_per_call": permute_bytes,
+                          "GB_per_s": permute_bytes / (perm_ms * 1e-3) / 1e9,
+                          "frac_hbm_peak": permute_bytes / (perm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "attn_fwd": {"ms_per_call": attn_ms, "flop_per_call": flops, "TFLOP_per_s": attn_tflops,
+                     "frac_mfma_peak": attn_tflops / PEAK_BF16_TFLOPS},
+    }
+
+    # plain copy of known size (for scaling HBM counters of a profiled run)
+    cp_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    cp_dst.copy_(cp_src)
+    torch.cuda.synchronize()
+    del cp_src, cp_dst
+
+    if not args.no_side:
+        components.update(ring_side(T, W, torch, dev, args.seed))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(grouped, S, Hl, D, args.cpu_rows)
+
+    line = {
+        "metric": "attention fwd TFLOP/s (bf16, causal S=32k, 8x128 heads); % of MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) rounded to bf16)",
+        "config": {"workload": "ulysses_share_32k: 3x shard_permute of 8 seq-shards [1,4096,64,128] bf16 to "
+                               "head group 0 [1,32768,8,128], then causal attn_fwd S=32768, 8 heads x 128",
+                   "batch": 1, "seq_len": S, "heads": Hl, "head_dim": D, "shards": P, "group": grp,
+                   "parallelism": "one GPU's Ulysses share"},
+        "frac_of_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd (attn_bf16_kernel<128, bf16>)",
+                     "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_kernel_ms": round(attn_ms, 4)},
+        "cpu_baseline": cpu,
+        "components": components,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def ring_side(T, W, torch, dev, seed):
+    """Ring share at the pages' shape: 8 chunk calls with fp32 partials + one 8-way merge."""
+    inp, p = W.workload_inputs(4, seed=seed + 1)
+    P, S, H, D = p["P"], p["S"], p["H"], p["D"]
+    Sc = S // P
+    qp = p["q_chunk"] * Sc
+    q = inp["q"].to(dev)
+    kc = [inp["k"][:, t * Sc:(t + 1) * Sc].contiguous().to(dev) for t in range(P)]
+    vc = [inp["v"][:, t * Sc:(t + 1) * Sc].contiguous().to(dev) for t in range(P)]
+    parts_o = [torch.empty((1, Sc, H, D), dtype=torch.float32, device=dev) for _ in range(P)]
+    parts_l = [torch.empty((1, H, Sc), dtype=torch.float32, device=dev) for _ in range(P)]
+    out = torch.empty((1, Sc, H, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((1, H, Sc), dtype=torch.float32, device=dev)
+
+    def run(rec=None):
+        if rec:
+            rec[0].record()
+        for t in range(P):
+            T.attn_fwd(q, kc[t], vc[t], causal=True, q_pos0=qp, k_pos0=t * Sc, out=parts_o[t], lse=parts_l[t])
+        if rec:
+            rec[1].record()
+        T.attn_merge_lse(parts_o, parts_l, out=out, lse_out=lse)
+        if rec:
+            rec[2].record()
+
+    for _ in range(3):
+        run()
+    reps = 20
+    recs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for r in recs:
+        run(r)
+    torch.cuda.synchronize()
+    attn_ms = sum(r[0].elapsed_time(r[1]) for r in recs) / reps
+    merge_ms = sum(r[1].elapsed_time(r[2]) for r in recs) / reps
+    flops = 4.0 * D * H * causal_pairs(Sc, S, qp, 0)
+    merge_bytes = P * (Sc * H * D * 4 + H * Sc * 4) + Sc * H * D * 2 + H * Sc * 4
+    return {
+        "ring_share_attn_8_chunks": {"ms": attn_ms, "flop": flops, "TFLOP_per_s": flops / (attn_ms * 1e-3) / 1e12,
+                                     "frac_mfma_peak": flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+        "attn_merge_lse_8way": {"us": merge_ms * 1e3, "bytes": merge_bytes,
+                                "GB_per_s": merge_bytes / (merge_ms * 1e-3) / 1e9,
+                                "frac_hbm_peak": merge_bytes / (merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+    }
+
+
+def cpu_baseline(grouped, S, H, D, n_rows):
+    """fp64 oracle on a sample of query rows of the same causal attention (all heads)."""
+    import torch
+
+    import oracle
+    q, k, v = (grouped[n].cpu() for n in ("q", "k", "v"))
+    # rows spread evenly over the sequence (later rows see more keys)
+    rows = torch.linspace(0, S - 1, n_rows).round().to(torch.int64)
+    pairs = int(sum(int(r) + 1 for r in rows)) * H
+    cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, causal=True, rows=rows, nthreads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": 4.0 * D * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": min(cores, n_rows), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"{n_rows} query rows evenly spaced over S={S} (all {H} heads, causal prefixes), "
+                      f"{pairs} visible pairs; fp64 two-pass oracle on {cores} host threads"}
+
+
+if __name__ == "__main__":
+    main()
