@@ -84,7 +84,7 @@ enum {
  * as in the data collator of "Support deepspeed sequence parallel"); they only
  * matter with THA_MASK_CAUSAL.  kv_len: device int32 [B], required iff
  * THA_MASK_KEY_PADDING (values are clamped to [0, Sk] on the device).
- * scale: multiplies q.k; pass 1/sqrt(D) for standard attention.
+ * scale: multiplies q.k, finite and > 0; pass 1/sqrt(D) for standard attention.
  *
  * Supported: in_dt = THA_BF16 with D = 64 or 128 (matrix-core path: bf16
  * products, fp32 accumulation and softmax, probabilities rounded to bf16 before
@@ -93,7 +93,7 @@ enum {
  * in_dt = THA_F32 with 1 <= D <= 256 (fp32 throughout).  out_dt may be THA_BF16
  * or THA_F32 in both cases (fp32 output keeps ring partials unrounded).
  * Errors: THA_ERR_INVALID for null q/k/v/o, non-positive sizes, unknown mask
- * bits, KEY_PADDING without kv_len, non-finite scale, |q_pos0| or |k_pos0| >=
+ * bits, KEY_PADDING without kv_len, scale not finite and positive, |q_pos0| or |k_pos0| >=
  * 2^62; THA_ERR_UNSUPPORTED for other dtypes / head dims.
  */
 THA_API int attn_fwd(const void* q, const void* k, const void* v, void* o, int out_dt, float* lse, int B, int Sq,

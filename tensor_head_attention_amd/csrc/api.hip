@@ -54,7 +54,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int out_dt, f
   if (B <= 0 || Sq <= 0 || Sk <= 0 || H <= 0 || D <= 0) return THA_ERR_INVALID;
   if (mask_flags & ~(unsigned)(THA_MASK_CAUSAL | THA_MASK_KEY_PADDING)) return THA_ERR_INVALID;
   if ((mask_flags & THA_MASK_KEY_PADDING) && !kv_len) return THA_ERR_INVALID;
-  if (!isfinite(scale)) return THA_ERR_INVALID;
+  if (!isfinite(scale) || !(scale > 0.f)) return THA_ERR_INVALID;
   if (q_pos0 >= kMaxPos || q_pos0 <= -kMaxPos || k_pos0 >= kMaxPos || k_pos0 <= -kMaxPos) return THA_ERR_INVALID;
   if (!dtype_ok(in_dt) || !dtype_ok(out_dt)) return THA_ERR_UNSUPPORTED;
   if ((int64_t)H * D > kMaxRowElems) return THA_ERR_UNSUPPORTED;

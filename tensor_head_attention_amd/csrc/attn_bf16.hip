@@ -11,7 +11,9 @@
 // Design (MI355X-first):
 //  * A workgroup of 4 wavefronts owns 128 query rows of one (batch, head);
 //    each wavefront owns 32 rows.  Keys stream through LDS in tiles of 64,
-//    double buffered, shared by the 4 wavefronts.
+//    double buffered and shared by the 4 wavefronts.  Tiles are copied
+//    global -> LDS by buffer_load ... lds (no register staging); the copy of
+//    tile t+1 runs while tile t is computed.
 //  * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    A = 32 keys x 16 dims of K (one 16-byte LDS read per lane), B = Q^T held
 //    in registers for the whole kernel.  In the accumulator layout a lane holds
@@ -22,11 +24,15 @@
 //    interleaved between the two half-waves) is matched by reading V^T with
 //    ds_read_b64_tr_b16, which transposes 16-bit elements out of the row-major
 //    V tile, so V never needs a transposed copy.
-//  * Online softmax in the exp2 domain with scale*log2(e) folded into one FMA;
-//    O^T is rescaled per lane (a lane's column is one query).
+//  * Online softmax in the exp2 domain with scale*log2(e) folded into one FMA.
+//    The running max is raised only when a row's new maximum exceeds it by
+//    more than 2^8 in probability terms (then the row's O and sum are rescaled);
+//    otherwise probabilities up to 256 are accumulated as they are.  The final
+//    normalisation divides by the matching sum, so the result is the same up to
+//    rounding and most tiles skip the rescale.
 //  * Masking (causal with global positions, key padding, sequence tails) is
 //    applied only on tiles that need it; tiles wholly in a wavefront's future
-//    are skipped.  Tail loads use buffer loads, which return zero out of range.
+//    are skipped.  Out-of-range loads return zero (buffer range checking).
 //  * Heaviest causal query tiles are launched first; consecutive workgroups
 //    take different heads of one query tile, so each head's workgroups land on
 //    one XCD (dispatch is round-robin over the 8 XCDs) and share its L2.
@@ -43,6 +49,7 @@ constexpr int kRowsPerWave = 32;
 constexpr int kBlockM = kWaves * kRowsPerWave;  // 128 query rows per workgroup
 constexpr int kBlockN = 64;                     // keys per LDS tile
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleLog2 = 8.0f;  // raise the running max only past a 2^8 growth
 
 // Swizzles of the 16-byte chunk index inside a tile row (row = key):
 //  K tile: read as 32 keys x one chunk per instruction -> spread keys over chunks.
@@ -60,13 +67,6 @@ __device__ __forceinline__ int v_swz(int row) {
     return 2 * r;  // 0, 2, 4, 6
 }
 
-template <int D>
-struct Smem {
-  static constexpr int kTileBytes = kBlockN * D * 2;
-  char k[2][kTileBytes];
-  char v[2][kTileBytes];
-};
-
 struct KernelArgs {
   const __bf16* q;
   const __bf16* k;
@@ -79,18 +79,22 @@ struct KernelArgs {
   long long q_pos0, k_pos0;
   float scale;       // natural-log scale (for lse)
   float scale_log2;  // scale * log2(e)
+  float rescale_raw; // kRescaleLog2 / scale_log2: raw-score growth that triggers a rescale
 };
 
 template <int D, typename OutT>
 __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(KernelArgs a) {
-  constexpr int kChunks = D / 8;           // 16-byte chunks per row
-  constexpr int kDSteps = D / 16;          // k-steps of the score product
-  constexpr int kDBlocks = D / 32;         // 32-row blocks of O^T
-  constexpr int kLoadIters = kBlockN * kChunks / kThreads;  // 16-byte loads per thread per tile
-  __shared__ __attribute__((aligned(16))) Smem<D> sm;
+  constexpr int kChunks = D / 8;                     // 16-byte chunks per row
+  constexpr int kDSteps = D / 16;                    // k-steps of the score product
+  constexpr int kDBlocks = D / 32;                   // 32-row blocks of O^T
+  constexpr int kTileBytes = kBlockN * D * 2;
+  constexpr int kRowsPerLoad = 1024 / (D * 2);       // tile rows written by one wave-wide 16 B load
+  constexpr int kLoadsPerWave = kTileBytes / 1024 / kWaves;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * 2 * kTileBytes];  // [buf][K|V][tile]
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int lq = lane & 31;   // this lane's query column within the wavefront
   const int hi = lane >> 5;   // half-wave
   const int BH = a.B * a.H;
@@ -118,6 +122,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(KernelArgs a) {
 
   // Q^T fragments: lane holds query q0 + lq, dims [16t + 8hi, +8) for each k-step t.
   const int q0 = q_first + wave * kRowsPerWave;
+  const bool wave_live = q0 < a.Sq;
   bf16x8 qf[kDSteps];
   {
     const int rows_valid = max(0, min(kRowsPerWave, a.Sq - q0));
@@ -131,30 +136,30 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(KernelArgs a) {
   const __bf16* kbase = a.k + ((int64_t)b * a.Sk * a.H + h) * D;
   const __bf16* vbase = a.v + ((int64_t)b * a.Sk * a.H + h) * D;
 
-  // Global -> register staging of one K/V tile: thread loads chunks id = tid + 256u.
-  i32x4 kst[kLoadIters], vst[kLoadIters];
-  auto load_tile = [&](int kt) {
+  // Per-lane global offsets of this wave's share of a tile copy: wave-wide load u fills
+  // LDS bytes [(wave*kLoadsPerWave + u) * 1024, +1024), lane i its 16 bytes at i*16, i.e.
+  // tile row r = (wave*kLoadsPerWave + u)*kRowsPerLoad + i/kChunks, stored chunk i%kChunks,
+  // which holds logical chunk (i%kChunks) ^ swizzle(r).
+  uint32_t koff[kLoadsPerWave], voff[kLoadsPerWave];
+#pragma unroll
+  for (int u = 0; u < kLoadsPerWave; ++u) {
+    const int r = (wave * kLoadsPerWave + u) * kRowsPerLoad + lane / kChunks;
+    const int p = lane % kChunks;
+    koff[u] = (uint32_t)r * row_bytes + (uint32_t)((p ^ k_swz<D>(r)) * 16);
+    voff[u] = (uint32_t)r * row_bytes + (uint32_t)((p ^ v_swz<D>(r)) * 16);
+  }
+  auto issue_tile = [&](int kt, int buf) {
     const int key0 = kt * kBlockN;
     const int rows_valid = min(kBlockN, kv_lim - key0);
     const uint32_t nbytes = (uint32_t)max(rows_valid, 0) * row_bytes;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + (int64_t)key0 * row_stride, nbytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + (int64_t)key0 * row_stride, nbytes);
+    const i32x4 rk = make_rsrc_words(kbase + (int64_t)key0 * row_stride, nbytes);
+    const i32x4 rv = make_rsrc_words(vbase + (int64_t)key0 * row_stride, nbytes);
+    const uint32_t kl = lds_addr(smem + (buf * 2 + 0) * kTileBytes + wave * kLoadsPerWave * 1024);
+    const uint32_t vl = lds_addr(smem + (buf * 2 + 1) * kTileBytes + wave * kLoadsPerWave * 1024);
 #pragma unroll
-    for (int u = 0; u < kLoadIters; ++u) {
-      const int id = tid + kThreads * u;
-      const int row = id / kChunks, c = id % kChunks;
-      const uint32_t off = (uint32_t)row * row_bytes + (uint32_t)c * 16;
-      kst[u] = buffer_load_16(rk, off);
-      vst[u] = buffer_load_16(rv, off);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < kLoadIters; ++u) {
-      const int id = tid + kThreads * u;
-      const int row = id / kChunks, c = id % kChunks;
-      *(i32x4*)(sm.k[buf] + row * (D * 2) + ((c ^ k_swz<D>(row)) * 16)) = kst[u];
-      *(i32x4*)(sm.v[buf] + row * (D * 2) + ((c ^ v_swz<D>(row)) * 16)) = vst[u];
+    for (int u = 0; u < kLoadsPerWave; ++u) {
+      buffer_load_lds_16(rk, kl + u * 1024, koff[u]);
+      buffer_load_lds_16(rv, vl + u * 1024, voff[u]);
     }
   };
 
@@ -163,21 +168,27 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(KernelArgs a) {
   for (int i = 0; i < kDBlocks; ++i)
 #pragma unroll
     for (int j = 0; j < 16; ++j) o_acc[i][j] = 0.f;
-  float m_run = -INFINITY;  // running max of raw scores q.k (this lane's query)
+  float m_run = -INFINITY;  // reference max of raw scores q.k (this lane's query)
   float l_run = 0.f;        // running sum over this half-wave's keys (exp2 domain)
 
   const long long q_pos = a.q_pos0 + q0 + lq;
-  const bool wave_live = q0 < a.Sq;
 
-  if (n_kt > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  // Per-lane LDS read offsets inside a tile.
+  // K (A operand of S^T): key row kb*32 + lq, logical chunk 2t + hi.
+  // V (transpose reads): lane (group g = lane/16, sl = lane%16) addresses row
+  // 16ks + 4hi + sl/4 (+8 for the second read) and dims 32db + 16(g&1) + 4(sl&3).
+  const int g = lane >> 4, sl = lane & 15;
+  const int vrow0 = 4 * hi + (sl >> 2);
+  const int vbyte_in = (sl & 1) * 8;
+  const int vchunk_base = 2 * (g & 1) + ((sl & 3) >> 1);
+
+  if (n_kt > 0) issue_tile(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
   for (int kt = 0; kt < n_kt; ++kt) {
     const int buf = kt & 1;
-    if (kt + 1 < n_kt) load_tile(kt + 1);
+    if (kt + 1 < n_kt) issue_tile(kt + 1, buf ^ 1);
 
     const int key0 = kt * kBlockN;
     // Wave-uniform tile classification.
@@ -189,6 +200,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(KernelArgs a) {
       if (first_kpos + kBlockN - 1 > a.q_pos0 + q0) need_mask = true;
     }
     if (!skip) {
+      const char* ks = smem + (buf * 2 + 0) * kTileBytes;
+      const lds_char* vs = (const lds_char*)(smem + (buf * 2 + 1) * kTileBytes);
       // ---- S^T = K Q^T for two 32-key blocks -------------------------------
       f32x16 s[2];
 #pragma unroll
@@ -196,7 +209,7 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(KernelArgs a) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) s[kb][j] = 0.f;
         const int row = kb * 32 + lq;
-        const char* krow = sm.k[buf] + row * (D * 2);
+        const char* krow = ks + row * (D * 2);
         const int sw = k_swz<D>(row);
 #pragma unroll
         for (int t = 0; t < kDSteps; ++t) {
@@ -216,64 +229,63 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(KernelArgs a) {
             if (hide) s[kb][j] = -INFINITY;
           }
       }
-      // ---- online softmax (exp2 domain) -------------------------------------
-      float mx = -INFINITY;
+      // ---- online softmax (exp2 domain, lazy rescale) -------------------------
+      float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int j = 2; j < 16; ++j) mx = fmaxf(mx, s[0][j]);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][j]);
+      for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[1][j]);
       mx = max_across_halves(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float neg_mc = -m_use * a.scale_log2;
-      const float alpha = __builtin_amdgcn_exp2f(fmaf(m_run, a.scale_log2, neg_mc));
-      m_run = m_new;
-      float rs = 0.f;
+      // Raise the reference max only when it grows past the threshold (or is still -inf).
+      const bool grow = mx > m_run + a.rescale_raw;
+      if (__builtin_amdgcn_ballot_w64(grow)) {  // wave-uniform
+        const float m_new = grow ? mx : m_run;
+        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * a.scale_log2) : 1.0f;
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int i = 0; i < kDBlocks; ++i)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[kb][j], a.scale_log2, neg_mc));
-          s[kb][j] = p;
-          rs += p;
-        }
-      l_run = fmaf(l_run, alpha, rs);
+          for (int j = 0; j < 16; ++j) o_acc[i][j] *= alpha;
+      }
+      const float neg_mc = m_run == -INFINITY ? 0.f : -m_run * a.scale_log2;
+      float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-      for (int i = 0; i < kDBlocks; ++i)
-#pragma unroll
-        for (int j = 0; j < 16; ++j) o_acc[i][j] *= alpha;
+      for (int j = 0; j < 16; ++j) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[0][j], a.scale_log2, neg_mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[1][j], a.scale_log2, neg_mc));
+        s[0][j] = p0;
+        s[1][j] = p1;
+        rs0 += p0;
+        rs1 += p1;
+      }
+      l_run += rs0 + rs1;
       // ---- P^T to bf16: B operands of the four 16-key steps -----------------
       bf16x8 pb[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int kb = ks >> 1, base = (ks & 1) * 8;
+      for (int ks4 = 0; ks4 < 4; ++ks4) {
+        const int kb = ks4 >> 1, base = (ks4 & 1) * 8;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[ks][e] = (__bf16)s[kb][base + e];
+        for (int e = 0; e < 8; ++e) pb[ks4][e] = (__bf16)s[kb][base + e];
       }
       // ---- O^T += V^T P^T ------------------------------------------------------
-      // Lane (group G = lane/16, s = lane%16) addresses row 16ks + 4hi + s/4 (+8 for the
-      // second read) and dims 32db + 16(G&1) + 4(s&3); the transpose read hands each
-      // lane 4 consecutive keys of one dim.
-      const int g = lane >> 4, sl = lane & 15;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int r0 = 16 * ks + 4 * hi + (sl >> 2);
+      for (int ks4 = 0; ks4 < 4; ++ks4) {
+        const int r0 = 16 * ks4 + vrow0;
         const int r1 = r0 + 8;
 #pragma unroll
         for (int db = 0; db < kDBlocks; ++db) {
-          const int c = 4 * db + 2 * (g & 1) + ((sl & 3) >> 1);
-          const int byte_in = (sl & 1) * 8;
-          const lds_char* vb = (const lds_char*)sm.v[buf];
+          const int c = 4 * db + vchunk_base;
           const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(vb + r0 * (D * 2) + ((c ^ v_swz<D>(r0)) * 16) + byte_in));
+              (lds_s16x4*)(vs + r0 * (D * 2) + ((c ^ v_swz<D>(r0)) * 16) + vbyte_in));
           const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(vb + r1 * (D * 2) + ((c ^ v_swz<D>(r1)) * 16) + byte_in));
+              (lds_s16x4*)(vs + r1 * (D * 2) + ((c ^ v_swz<D>(r1)) * 16) + vbyte_in));
           const s16x8 t = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
-          o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, t), pb[ks], o_acc[db], 0, 0, 0);
+          o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, t), pb[ks4], o_acc[db], 0, 0, 0);
         }
       }
     }
-    if (kt + 1 < n_kt) store_tile(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's share of tile kt+1 has landed in LDS
     __syncthreads();
   }
 
@@ -318,6 +330,7 @@ hipError_t launch_d(const AttnArgs& x, hipStream_t st) {
   a.q_pos0 = x.q_pos0, a.k_pos0 = x.k_pos0;
   a.scale = x.scale;
   a.scale_log2 = x.scale * kLog2e;
+  a.rescale_raw = kRescaleLog2 / a.scale_log2;
   const int64_t n_qt = (x.Sq + kBlockM - 1) / kBlockM;
   const int64_t blocks = n_qt * x.B * x.H;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;

@@ -23,8 +23,45 @@ typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
 // 32-bit data format, no index stride.  Loads at offsets >= num_records return zero.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 
+// The base and size must be wave-uniform; readfirstlane states that to the compiler so the
+// descriptor lives in SGPRs (a descriptor it believes divergent costs a loop per load).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, kBufferRsrcWord3);
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  void* up = (void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(up, (short)0, (int)__builtin_amdgcn_readfirstlane(num_bytes),
+                                           kBufferRsrcWord3);
+}
+
+// The same descriptor as four raw dwords (for the inline-asm copy below).
+__device__ __forceinline__ i32x4 make_rsrc_words(const void* base, uint32_t num_bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  i32x4 r;
+  r[0] = (int)__builtin_amdgcn_readfirstlane((uint32_t)p);
+  r[1] = (int)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32) & 0xffffu);  // stride 0
+  r[2] = (int)__builtin_amdgcn_readfirstlane(num_bytes);
+  r[3] = kBufferRsrcWord3;
+  return r;
+}
+
+// Direct global -> LDS copy (buffer_load_dwordx4 ... lds): lane i's 16 bytes, read at byte
+// offset voff of the buffer (zero when out of range), land at LDS byte lds_base + 16*i.
+// lds_base must be wave-uniform.  Written as inline asm so the compiler does not order later
+// LDS reads behind it; the caller waits (vmcnt) before a barrier that publishes the data.
+// The kernels that use it issue no other M0-based instruction.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is set inside the statement on purpose
+__device__ __forceinline__ void buffer_load_lds_16(i32x4 rsrc, uint32_t lds_base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_char*)p);
 }
 
 __device__ __forceinline__ i32x4 buffer_load_16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {

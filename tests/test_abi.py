@@ -73,6 +73,8 @@ def test_attn_fwd_validation(lib):
     assert _attn(lib, flags=T.THA_MASK_KEY_PADDING) == E  # key padding without kv_len
     assert _attn(lib, scale=float("inf")) == E
     assert _attn(lib, scale=float("nan")) == E
+    assert _attn(lib, scale=0.0) == E
+    assert _attn(lib, scale=-0.5) == E
     assert _attn(lib, qp=1 << 62) == E
     assert _attn(lib, kp=-(1 << 62)) == E
     assert _attn(lib, in_dt=5) == U
