@@ -44,6 +44,23 @@ def causal_pairs(Sq: int, Sk: int, q_pos0: int, k_pos0: int) -> int:
     return tot
 
 
+def attn_traffic():
+    """HBM bytes per attn_fwd dispatch from the committed rocprofv3 FETCH/WRITE summary, or None
+    when the kernel source has changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "attn_fwd_ulysses32k_hbm_traffic.txt")
+    src = os.path.join(ROOT, "tensor_head_attention_amd", "csrc", "attn_bf16.hip")
+    try:
+        txt = open(path).read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    fields = dict(l.split(": ", 1) for l in txt.splitlines() if ": " in l)
+    if fields.get("attn_bf16.hip sha256 prefix", "").strip() != sha:
+        return None
+    return float(fields["attn_fwd traffic_bytes_per_dispatch"])
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,7 +175,7 @@ def main():
         "frac_of_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "roofline": {"bound": "mfma", "kernel": "attn_fwd (attn_bf16_kernel<128, bf16>)",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": attn_traffic(),
                      "avg_kernel_ms": round(attn_ms, 4)},
         "cpu_baseline": cpu,
         "components": components,
