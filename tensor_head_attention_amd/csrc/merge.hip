@@ -5,12 +5,9 @@
 //   M = max_k lse_k; w_k = exp(lse_k - M); o = sum_k w_k o_k / sum_k w_k;
 //   lse = M + log(sum_k w_k); all parts empty (-inf) -> o = 0, lse = -inf.
 //
-// HBM-bound streaming kernel.  A row (b, s, h) of D elements is handled by
-// `lanes` lanes of one wavefront (a power of two dividing 64), each owning
-// chunks of kVec consecutive elements.  Keeping a row inside one wavefront
-// makes in-place use safe: every lane reads the row's lse values before the
-// row's single lse store, and each output element is written by the lane
-// that read it.
+// HBM-bound streaming kernel: every partial is read once (non-temporal) and
+// the result written once.  See the two kernels below for how in-place use
+// stays race-free.
 #include "device_common.h"
 #include "tha_kernels.h"
 
@@ -25,12 +22,20 @@ struct Vec4;
 template <>
 struct Vec4<float> {
   __device__ static f32x4 load(const void* p, int64_t i) { return *(const f32x4*)((const float*)p + i); }
+  __device__ static f32x4 load_nt(const void* p, int64_t i) {
+    return __builtin_nontemporal_load((const f32x4*)((const float*)p + i));
+  }
   __device__ static void store(void* p, int64_t i, f32x4 v) { *(f32x4*)((float*)p + i) = v; }
 };
 template <>
 struct Vec4<__bf16> {
   __device__ static f32x4 load(const void* p, int64_t i) {
     bf16x4 v = *(const bf16x4*)((const __bf16*)p + i);
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+  }
+  __device__ static f32x4 load_nt(const void* p, int64_t i) {
+    const uint64_t u = __builtin_nontemporal_load((const uint64_t*)((const __bf16*)p + i));
+    bf16x4 v = __builtin_bit_cast(bf16x4, u);
     return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
   }
   __device__ static void store(void* p, int64_t i, f32x4 v) {
@@ -48,61 +53,95 @@ __device__ __forceinline__ void store1(void* p, int64_t i, float v) {
   ((T*)p)[i] = (T)v;
 }
 
-// kVec = 4: D % 4 == 0 and 8/16-byte aligned rows; kVec = 1: any D.
-template <typename PartT, typename OutT, int kVec>
-__global__ void __launch_bounds__(kThreads) merge_kernel(PartPtrs parts, int n, void* o_out, float* lse_out,
-                                                        int64_t rows, int S, int H, int D, int lanes_log2) {
+// Vector path (D % 4 == 0, D <= 1024, 8/16-byte aligned rows): each thread owns one chunk of 4
+// consecutive elements of one row; a row is `lanes` consecutive threads of the block (lanes a power
+// of two, <= 256).  Every thread reads the row's lse values before the block barrier and the row's
+// single lse store comes after it, so lse_out may alias lse_parts[0]; each output element is
+// written by the thread that read it, so o_out may alias o_parts[0].
+template <typename PartT, typename OutT>
+__global__ void __launch_bounds__(kThreads) merge_vec_kernel(PartPtrs parts, int n, void* o_out, float* lse_out,
+                                                            int64_t rows, int S, int H, int D, int lanes_log2) {
   const int lanes = 1 << lanes_log2;
-  const int rows_per_block = kThreads >> lanes_log2;
   const int lane_in_row = threadIdx.x & (lanes - 1);
-  const int64_t row = (int64_t)blockIdx.x * rows_per_block + (threadIdx.x >> lanes_log2);
+  const int64_t row = (int64_t)blockIdx.x * (kThreads >> lanes_log2) + (threadIdx.x >> lanes_log2);
+  const bool live = row < rows;
+  int64_t li = 0;
+  float M = -INFINITY;
+  if (live) {
+    // row = (b*S + s)*H + h  ->  lse index (b*H + h)*S + s
+    const int64_t bs = row / H;
+    const int h = (int)(row - bs * H);
+    const int64_t b = bs / S;
+    const int s = (int)(bs - b * S);
+    li = (b * H + h) * S + s;
+    for (int k = 0; k < n; ++k) M = fmaxf(M, parts.lse[k][li]);
+  }
+  __syncthreads();  // all lse reads of the block precede its lse writes (in-place safety)
+  if (!live) return;
+  const int c = lane_in_row * 4;
+  const int64_t off = row * D + c;
+  if (M == -INFINITY) {
+    if (c < D) Vec4<OutT>::store(o_out, off, f32x4{0.f, 0.f, 0.f, 0.f});
+    if (lse_out && lane_in_row == 0) lse_out[li] = -INFINITY;
+    return;
+  }
+  // Parts in chunks of 8: all loads of a chunk in flight before its weights are applied.
+  constexpr int kChunk = 8;
+  float W = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < n; k0 += kChunk) {
+    const int kn = min(kChunk, n - k0);
+    f32x4 x[kChunk];
+    float w[kChunk];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      w[u] = 0.f;
+      if (u < kn) {
+        if (c < D) x[u] = Vec4<PartT>::load_nt(parts.o[k0 + u], off);
+        w[u] = expf(parts.lse[k0 + u][li] - M);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u)
+      if (u < kn) {
+        W += w[u];
+        if (c < D) acc += x[u] * w[u];
+      }
+  }
+  if (c < D) Vec4<OutT>::store(o_out, off, acc * (1.0f / W));
+  if (lse_out && lane_in_row == 0) lse_out[li] = M + logf(W);
+}
+
+// Scalar path (any D): a row is handled by `lanes` lanes of one wavefront (a power of two
+// dividing 64), each owning elements lane_in_row, lane_in_row + lanes, ...; a row stays inside one
+// wavefront, so every lane reads the row's lse values before the row's single lse store.
+template <typename PartT, typename OutT>
+__global__ void __launch_bounds__(kThreads) merge_scalar_kernel(PartPtrs parts, int n, void* o_out, float* lse_out,
+                                                               int64_t rows, int S, int H, int D, int lanes_log2) {
+  const int lanes = 1 << lanes_log2;
+  const int lane_in_row = threadIdx.x & (lanes - 1);
+  const int64_t row = (int64_t)blockIdx.x * (kThreads >> lanes_log2) + (threadIdx.x >> lanes_log2);
   if (row >= rows) return;  // whole rows leave together
-  // row = (b*S + s)*H + h  ->  lse index (b*H + h)*S + s
   const int64_t bs = row / H;
   const int h = (int)(row - bs * H);
   const int64_t b = bs / S;
   const int s = (int)(bs - b * S);
   const int64_t li = (b * H + h) * S + s;
-
   float M = -INFINITY;
   for (int k = 0; k < n; ++k) M = fmaxf(M, parts.lse[k][li]);
   const int64_t obase = row * D;
   if (M == -INFINITY) {
-    for (int c = lane_in_row * kVec; c < D; c += lanes * kVec) {
-      if constexpr (kVec == 4)
-        Vec4<OutT>::store(o_out, obase + c, f32x4{0.f, 0.f, 0.f, 0.f});
-      else
-        store1<OutT>(o_out, obase + c, 0.f);
-    }
+    for (int c = lane_in_row; c < D; c += lanes) store1<OutT>(o_out, obase + c, 0.f);
     if (lse_out && lane_in_row == 0) lse_out[li] = -INFINITY;
     return;
   }
   float W = 0.f;
   for (int k = 0; k < n; ++k) W += expf(parts.lse[k][li] - M);
   const float inv_w = 1.0f / W;
-  for (int c = lane_in_row * kVec; c < D; c += lanes * kVec) {
-    if constexpr (kVec == 4) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      int k = 0;
-      for (; k + 4 <= n; k += 4) {  // four independent loads in flight
-        f32x4 x0 = Vec4<PartT>::load(parts.o[k], obase + c);
-        f32x4 x1 = Vec4<PartT>::load(parts.o[k + 1], obase + c);
-        f32x4 x2 = Vec4<PartT>::load(parts.o[k + 2], obase + c);
-        f32x4 x3 = Vec4<PartT>::load(parts.o[k + 3], obase + c);
-        const float w0 = expf(parts.lse[k][li] - M) * inv_w, w1 = expf(parts.lse[k + 1][li] - M) * inv_w;
-        const float w2 = expf(parts.lse[k + 2][li] - M) * inv_w, w3 = expf(parts.lse[k + 3][li] - M) * inv_w;
-        acc += x0 * w0;
-        acc += x1 * w1;
-        acc += x2 * w2;
-        acc += x3 * w3;
-      }
-      for (; k < n; ++k) acc += Vec4<PartT>::load(parts.o[k], obase + c) * (expf(parts.lse[k][li] - M) * inv_w);
-      Vec4<OutT>::store(o_out, obase + c, acc);
-    } else {
-      float acc = 0.f;
-      for (int k = 0; k < n; ++k) acc += load1<PartT>(parts.o[k], obase + c) * (expf(parts.lse[k][li] - M) * inv_w);
-      store1<OutT>(o_out, obase + c, acc);
-    }
+  for (int c = lane_in_row; c < D; c += lanes) {
+    float acc = 0.f;
+    for (int k = 0; k < n; ++k) acc += load1<PartT>(parts.o[k], obase + c) * (expf(parts.lse[k][li] - M) * inv_w);
+    store1<OutT>(o_out, obase + c, acc);
   }
   if (lse_out && lane_in_row == 0) lse_out[li] = M + logf(W);
 }
@@ -111,18 +150,19 @@ template <typename PartT, typename OutT>
 hipError_t launch_typed(int n, const PartPtrs& parts, void* o_out, float* lse_out, int B, int S, int H, int D,
                         bool vec, hipStream_t st) {
   const int chunks = vec ? D / 4 : D;
+  const int max_lanes_log2 = vec ? 8 : 6;
   int lanes_log2 = 0;
-  while ((1 << lanes_log2) < chunks && lanes_log2 < 6) ++lanes_log2;
+  while ((1 << lanes_log2) < chunks && lanes_log2 < max_lanes_log2) ++lanes_log2;
   const int64_t rows = (int64_t)B * S * H;
   const int rows_per_block = kThreads >> lanes_log2;
   const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (vec)
-    hipLaunchKernelGGL((merge_kernel<PartT, OutT, 4>), dim3((unsigned)blocks), dim3(kThreads), 0, st, parts, n, o_out,
+    hipLaunchKernelGGL((merge_vec_kernel<PartT, OutT>), dim3((unsigned)blocks), dim3(kThreads), 0, st, parts, n, o_out,
                        lse_out, rows, S, H, D, lanes_log2);
   else
-    hipLaunchKernelGGL((merge_kernel<PartT, OutT, 1>), dim3((unsigned)blocks), dim3(kThreads), 0, st, parts, n, o_out,
-                       lse_out, rows, S, H, D, lanes_log2);
+    hipLaunchKernelGGL((merge_scalar_kernel<PartT, OutT>), dim3((unsigned)blocks), dim3(kThreads), 0, st, parts, n,
+                       o_out, lse_out, rows, S, H, D, lanes_log2);
   return hipGetLastError();
 }
 
@@ -131,7 +171,7 @@ hipError_t launch_typed(int n, const PartPtrs& parts, void* o_out, float* lse_ou
 hipError_t launch_merge_lse(int n, const PartPtrs& parts, int part_dt, void* o_out, int out_dt, float* lse_out, int B,
                             int S, int H, int D, hipStream_t st) {
   const int pb = part_dt == THA_F32 ? 4 : 2, ob = out_dt == THA_F32 ? 4 : 2;
-  bool vec = (D % 4 == 0) && ((uintptr_t)o_out % (4 * ob) == 0);
+  bool vec = (D % 4 == 0) && D <= 1024 && ((uintptr_t)o_out % (4 * ob) == 0);
   for (int k = 0; k < n && vec; ++k) vec = ((uintptr_t)parts.o[k] % (4 * pb) == 0);
   if (part_dt == THA_F32 && out_dt == THA_F32)
     return launch_typed<float, float>(n, parts, o_out, lse_out, B, S, H, D, vec, st);

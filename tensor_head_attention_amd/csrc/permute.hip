@@ -19,48 +19,34 @@ namespace tha {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kVecPerThread = 4;  // independent 16 B loads in flight per thread
 
-// Vector path.  Thread item index idx (of 16 B) in the grouped tensor [B, S, H/P, D]
-// maps to token (b, s) = idx / run_vecs and vector v = idx % run_vecs.
+// Vector path: one 16-byte vector per thread (the most loads in flight across the chip, which
+// measured fastest for this strided-read / contiguous-write mix), non-temporal both ways since
+// every byte is touched once.  Item idx (of 16 B) in the grouped tensor [B, S, H/P, D] maps to
+// token (b, s) = idx / run_vecs and vector v = idx % run_vecs.
 template <bool kToGroup>
 __global__ void __launch_bounds__(kThreads) permute_vec_kernel(ShardPtrs shards, char* grouped, int64_t total_vecs,
                                                               uint32_t run_vecs, uint32_t run_shift, int S, int Sl,
                                                               int64_t shard_row_bytes, int64_t group_off_bytes) {
-  const int64_t base = ((int64_t)blockIdx.x * kThreads * kVecPerThread) + threadIdx.x;
-  i32x4 buf[kVecPerThread];
-  int64_t gidx[kVecPerThread];
-  const char* src[kVecPerThread];
-  char* dst[kVecPerThread];
-#pragma unroll
-  for (int u = 0; u < kVecPerThread; ++u) {
-    const int64_t idx = base + (int64_t)u * kThreads;
-    gidx[u] = idx;
-    if (idx >= total_vecs) continue;
-    int64_t tok;
-    uint32_t v;
-    if (run_shift != 0xffffffffu) {  // power-of-two run length
-      tok = idx >> run_shift;
-      v = (uint32_t)(idx & (run_vecs - 1));
-    } else {
-      tok = idx / run_vecs;
-      v = (uint32_t)(idx - tok * run_vecs);
-    }
-    const int64_t b = tok / S;
-    const int s = (int)(tok - b * S);
-    const int i = s / Sl;
-    const int t = s - i * Sl;
-    char* shard_p = (char*)shards.p[i] + (b * Sl + t) * shard_row_bytes + group_off_bytes + (int64_t)v * 16;
-    char* group_p = grouped + idx * 16;
-    src[u] = kToGroup ? shard_p : group_p;
-    dst[u] = kToGroup ? group_p : shard_p;
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= total_vecs) return;
+  int64_t tok;
+  uint32_t v;
+  if (run_shift != 0xffffffffu) {  // power-of-two run length
+    tok = idx >> run_shift;
+    v = (uint32_t)(idx & (run_vecs - 1));
+  } else {
+    tok = idx / run_vecs;
+    v = (uint32_t)(idx - tok * run_vecs);
   }
-#pragma unroll
-  for (int u = 0; u < kVecPerThread; ++u)
-    if (gidx[u] < total_vecs) buf[u] = __builtin_nontemporal_load((const i32x4*)src[u]);
-#pragma unroll
-  for (int u = 0; u < kVecPerThread; ++u)
-    if (gidx[u] < total_vecs) __builtin_nontemporal_store(buf[u], (i32x4*)dst[u]);
+  const int64_t b = tok / S;
+  const int s = (int)(tok - b * S);
+  const int i = s / Sl;
+  const int t = s - i * Sl;
+  char* shard_p = (char*)shards.p[i] + (b * Sl + t) * shard_row_bytes + group_off_bytes + (int64_t)v * 16;
+  char* group_p = grouped + idx * 16;
+  const i32x4 x = __builtin_nontemporal_load((const i32x4*)(kToGroup ? shard_p : group_p));
+  __builtin_nontemporal_store(x, (i32x4*)(kToGroup ? group_p : shard_p));
 }
 
 // Element-wise fallback for unaligned or odd-sized runs.
@@ -113,8 +99,7 @@ hipError_t launch_permute(const ShardPtrs& sp, int P, int group, void* grouped, 
       while ((1u << shift) < run_vecs) ++shift;
     }
     const int64_t total = tokens * run_vecs;
-    const int64_t per_block = (int64_t)kThreads * kVecPerThread;
-    const int64_t blocks = (total + per_block - 1) / per_block;
+    const int64_t blocks = (total + kThreads - 1) / kThreads;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL((permute_vec_kernel<kToGroup>), dim3((unsigned)blocks), dim3(kThreads), 0, st, sp,
                        (char*)grouped, total, run_vecs, shift, S, Sl, row_bytes, off_bytes);

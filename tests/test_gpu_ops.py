@@ -77,7 +77,8 @@ def _parts(n, B, S, H, D, seed, part_dtype=torch.float32, spread=80.0):
 
 
 @pytest.mark.parametrize("n,B,S,H,D", [(1, 1, 50, 2, 128), (2, 2, 33, 3, 128), (8, 1, 100, 8, 128),
-                                       (5, 1, 17, 2, 64), (3, 2, 9, 2, 6), (64, 1, 4, 1, 8)])
+                                       (5, 1, 17, 2, 64), (3, 2, 9, 2, 6), (64, 1, 4, 1, 8), (9, 1, 5, 2, 12),
+                                       (2, 1, 3, 2, 1024), (2, 1, 3, 1, 1028)])
 @pytest.mark.parametrize("part_dt,out_dt", [(torch.float32, torch.bfloat16), (torch.float32, torch.float32),
                                             (torch.bfloat16, torch.bfloat16)])
 def test_merge_matches_oracle(n, B, S, H, D, part_dt, out_dt):
