@@ -41,9 +41,17 @@ def _compile(src: str) -> str:
     return obj
 
 
+def generate_sources() -> None:
+    """Regenerate the hand-scheduled attention loop (attn_loop_d128.inc) from its generator."""
+    r = subprocess.run([sys.executable, os.path.join(CSRC, "gen_attn_loop.py")], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gen_attn_loop.py failed:\n{r.stdout}{r.stderr}")
+
+
 def build_library(jobs: int = 8) -> str:
-    """Compile every HIP source and link libtha.so (always rebuilds)."""
+    """Generate the asm loop, compile every HIP source and link libtha.so (always rebuilds)."""
     os.makedirs(BUILD, exist_ok=True)
+    generate_sources()
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     with ThreadPoolExecutor(max_workers=min(jobs, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))

@@ -8,6 +8,9 @@
 // and the cast of the probabilities back to the input type before the product
 // with V).
 //
+// This file's kernel serves head size 64; head size 128 goes to the software-pipelined
+// kernel of attn_bf16_d128.hip, which keeps the same layout and work split.
+//
 // Design (MI355X-first):
 //  * A workgroup of 4 wavefronts owns 128 query rows of one (batch, head);
 //    each wavefront owns 32 rows.  Keys stream through LDS in tiles of 64,
@@ -344,7 +347,7 @@ hipError_t launch_d(const AttnArgs& x, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
-  if (a.D == 128) return launch_d<128>(a, st);
+  if (a.D == 128) return launch_attn_bf16_d128(a, st);  // software-pipelined kernel
   if (a.D == 64) return launch_d<64>(a, st);
   return hipErrorInvalidValue;
 }

@@ -1,0 +1,360 @@
+#!/usr/bin/env python3
+"""Writes attn_loop_d128.inc: the main loop of the pipelined bf16 attention kernel (D = 128) as the
+text of one inline-asm statement, scheduled by hand for CDNA4 (gfx950).  The build runs this script
+before compiling attn_bf16_d128.hip, which defines the operands and the C++ around the loop.
+
+Per 64-key tile t, for a wavefront of 32 query rows (the kernel source explains the layout):
+  phase A: S(t+1) = K(t+1) Q^T, 16 v_mfma_f32_32x32x16_bf16, each followed by a slice of the
+           softmax of tile t: p = 2^(s*c + neg_mc), the row sum, and the bf16 packing of P;
+  phase B: O^T += V(t)^T P(t)^T, 16 MFMAs, each followed by a slice of the mask and row max of
+           tile t+1;
+  then the lazy running-max update, the copies of later tiles into LDS, and the barrier.
+Fragments are read from LDS three MFMAs ahead; each wait covers exactly the fragment needed.
+
+Register map (physical VGPRs, pinned by the operand constraints):
+  O^T[db]   v[192+16db : 207+16db]      (fp32 accumulators, 4 blocks of 32 dims)
+  S set A   v[128:159], S set B v[96:127] (scores of the current / next tile, alternating)
+  Q^T[t]    v[64+4t : 67+4t]            (bf16 fragments, loaded once)
+  K frags   v[48:63], V frags v[32:47]   (rotating prefetch buffers)
+  v31 row sum, v30 row max, v29 -inf, v28/v27 temporaries; s[80:99] scalar temporaries.
+Wait states: every VALU read of an MFMA result, and every MFMA read of a VALU result, is separated
+from the writer by at least eight MFMAs or three s_nop 7, so no hazard needs hardware interlocks.
+"""
+import sys
+
+O_BASE, SA_BASE, SB_BASE, Q_BASE, K_BASE, V_BASE = 192, 128, 96, 64, 48, 32
+RS, MX, NEGINF, T0, ALPHA = 31, 30, 29, 28, 27
+# scalar temporaries (clobbered)
+S_T, S_T1, S_KEY, S_ROWS, S_TMP = 80, 81, 82, 83, 84
+S_KP, S_VP = 86, 88          # running 64-bit K/V tile pointers (pairs)
+S_KR, S_VR = 92, 96          # buffer resource quads (aligned)
+TILE_BYTES = 16384
+
+
+def vr(a, n=1):
+    return f"v{a}" if n == 1 else f"v[{a}:{a + n - 1}]"
+
+
+def sr(a, n=1):
+    return f"s{a}" if n == 1 else f"s[{a}:{a + n - 1}]"
+
+
+class Asm:
+    def __init__(self):
+        self.lines = []
+        self.lds_ops = 0
+
+    def e(self, s):
+        self.lines.append(s)
+
+    def lds(self, s):
+        self.e(s)
+        self.lds_ops += 1
+        return self.lds_ops - 1
+
+    def wait_for(self, op):
+        n = max(0, min(self.lds_ops - 1 - op, 15))
+        self.e(f"s_waitcnt lgkmcnt({n})")
+
+
+def block(A, cur_base, nxt_base, kbuf, vbuf, has_next, mask_next):
+    """One tile: phase A (QK of tile t+1 || probabilities of tile t), phase B (PV of t || mask+max of t+1)."""
+    A.lds_ops = 0
+    A.e("s_waitcnt lgkmcnt(0)")
+    A.e(f"v_mov_b32 {vr(RS)}, 0")
+    if mask_next:
+        A.e(f"v_mov_b32 {vr(NEGINF)}, 0xff800000")
+        # per-lane bound for tile t+1: hide key c (in-tile, minus 4hi) iff c >= base2 - key0
+        A.e(f"v_subrev_u32_e32 {vr(T0)}, {sr(S_KEY)}, %[base2]")
+
+    def cur(kb, r):
+        return cur_base + 16 * kb + r
+
+    def nxt(kb, r):
+        return nxt_base + 16 * kb + r
+
+    k_ops = {}
+
+    def issue_k(i):
+        kb, tt = divmod(i, 8)
+        off = kbuf * TILE_BYTES + kb * 8192
+        k_ops[i] = A.lds(f"ds_read_b128 {vr(K_BASE + 4 * (i % 4), 4)}, %[ka{tt}] offset:{off}")
+
+    elems = [(kb, r) for kb in range(2) for r in range(16)]
+    slots = []
+    for i in range(16):
+        (ka, ra), (kb_, rb) = elems[2 * i], elems[2 * i + 1]
+        ea, eb = cur(ka, ra), cur(kb_, rb)
+        slots.append([
+            f"v_fma_f32 {vr(ea)}, {vr(ea)}, %[c], %[nmc]",
+            f"v_fma_f32 {vr(eb)}, {vr(eb)}, %[c], %[nmc]",
+            f"v_exp_f32_e32 {vr(ea)}, {vr(ea)}",
+            f"v_exp_f32_e32 {vr(eb)}, {vr(eb)}",
+            f"v_add_f32_e32 {vr(RS)}, {vr(RS)}, {vr(ea)}",
+            f"v_add_f32_e32 {vr(RS)}, {vr(RS)}, {vr(eb)}",
+        ])
+    for g in range(4):
+        kb, h = divmod(g, 2)
+        for m in range(4):
+            d = cur(kb, 8 * h + m)
+            s0, s1 = cur(kb, 8 * h + 2 * m), cur(kb, 8 * h + 2 * m + 1)
+            slot = min(4 * g + 4 + m, 15)
+            slots[slot].append(f"v_cvt_pk_bf16_f32 {vr(d)}, {vr(s0)}, {vr(s1)}")
+
+    if has_next:
+        for i in range(3):
+            issue_k(i)
+        for i in range(16):
+            if i + 3 < 16:
+                issue_k(i + 3)
+            kb, tt = divmod(i, 8)
+            A.wait_for(k_ops[i])
+            src2 = "0" if tt == 0 else vr(nxt(kb, 0), 16)
+            A.e(f"v_mfma_f32_32x32x16_bf16 {vr(nxt(kb, 0), 16)}, {vr(K_BASE + 4 * (i % 4), 4)}, "
+                f"{vr(Q_BASE + 4 * tt, 4)}, {src2}")
+            for op in slots[i]:
+                A.e(op)
+    else:
+        for i in range(16):
+            for op in slots[i]:
+                A.e(op)
+
+    v_ops = {}
+
+    def issue_v(i):
+        ks, db = divmod(i, 4)
+        base = V_BASE + 4 * (i % 4)
+        off = vbuf * TILE_BYTES + ks * 4096
+        A.lds(f"ds_read_b64_tr_b16 {vr(base, 2)}, %[va{db}] offset:{off}")
+        v_ops[i] = A.lds(f"ds_read_b64_tr_b16 {vr(base + 2, 2)}, %[va{db}] offset:{off + 2048}")
+
+    bsl = [[] for _ in range(16)]
+    if has_next:
+        for kb in range(2):
+            for r in range(16):
+                slot = kb * 8 + r // 2
+                e_ = nxt(kb, r)
+                if mask_next:
+                    cconst = kb * 32 + (r >> 2) * 8 + (r & 3)
+                    bsl[slot].append(f"v_cmp_ge_i32_e32 vcc, {cconst}, {vr(T0)}")
+                    bsl[slot].append(f"v_cndmask_b32_e32 {vr(e_)}, {vr(e_)}, {vr(NEGINF)}, vcc")
+        pairs = [(nxt(kb, r), nxt(kb, r + 1)) for kb in range(2) for r in range(0, 16, 2)]
+        for pi, (ea, eb) in enumerate(pairs):
+            if pi == 0:
+                bsl[pi].append(f"v_max_f32_e32 {vr(MX)}, {vr(ea)}, {vr(eb)}")
+            else:
+                bsl[pi].append(f"v_max3_f32 {vr(MX)}, {vr(MX)}, {vr(ea)}, {vr(eb)}")
+
+    for i in range(3):
+        issue_v(i)
+    for i in range(16):
+        if i + 3 < 16:
+            issue_v(i + 3)
+        ks, db = divmod(i, 4)
+        kb, h = divmod(ks, 2)
+        A.wait_for(v_ops[i])
+        A.e(f"v_mfma_f32_32x32x16_bf16 {vr(O_BASE + 16 * db, 16)}, {vr(V_BASE + 4 * (i % 4), 4)}, "
+            f"{vr(cur(kb, 8 * h), 4)}, {vr(O_BASE + 16 * db, 16)}")
+        for op in bsl[i]:
+            A.e(op)
+
+    if has_next:
+        A.e("s_nop 1")
+        A.e(f"v_mov_b32 {vr(T0)}, {vr(MX)}")
+        A.e("s_nop 1")
+        A.e(f"v_permlane32_swap_b32_e32 {vr(T0)}, {vr(MX)}")
+        A.e("s_nop 1")
+        A.e(f"v_max_f32_e32 {vr(MX)}, {vr(T0)}, {vr(MX)}")
+    A.e(f"v_add_f32_e32 %[lrun], %[lrun], {vr(RS)}")
+    # MFMA results (O) may be read by VALU right after: keep >= 24 wait states
+    A.e("s_nop 7")
+    A.e("s_nop 7")
+    A.e("s_nop 7")
+
+
+def rescale(A, lbl):
+    """Lazy running-max update from MX (row max of the next tile), then neg_mc."""
+    A.e(f"v_add_f32_e32 {vr(T0)}, %[thr], %[mrun]")
+    A.e(f"v_cmp_gt_f32_e32 vcc, {vr(MX)}, {vr(T0)}")
+    A.e("s_nop 4")                                                       # vcc written by VALU -> vccz branch
+    A.e(f"s_cbranch_vccz {lbl}")
+    A.e(f"v_cndmask_b32_e32 {vr(T0)}, %[mrun], {vr(MX)}, vcc")        # m_new
+    A.e(f"v_sub_f32_e32 {vr(ALPHA)}, %[mrun], {vr(T0)}")
+    A.e(f"v_mul_f32_e32 {vr(ALPHA)}, %[c], {vr(ALPHA)}")
+    A.e(f"v_exp_f32_e32 {vr(ALPHA)}, {vr(ALPHA)}")
+    A.e("s_nop 0")                                                       # transcendental result -> VALU
+    A.e(f"v_cndmask_b32_e64 {vr(ALPHA)}, 1.0, {vr(ALPHA)}, vcc")      # lanes that keep their max: 1
+    A.e(f"v_mov_b32 %[mrun], {vr(T0)}")
+    A.e(f"v_mul_f32_e32 %[lrun], %[lrun], {vr(ALPHA)}")
+    for r in range(64):
+        A.e(f"v_mul_f32_e32 {vr(O_BASE + r)}, {vr(O_BASE + r)}, {vr(ALPHA)}")
+    A.e("s_nop 1")
+    A.e(f"{lbl}:")
+    A.e(f"v_mul_f32_e64 %[nmc], -%[mrun], %[c]")
+    A.e(f"v_cmp_eq_f32_e32 vcc, 0xff800000, %[mrun]")
+    A.e(f"v_cndmask_b32_e64 %[nmc], %[nmc], 0, vcc")
+
+
+def dma(A, which, buf, lbl_skip, ahead):
+    """Copy tile (t + ahead) of K or V into LDS buffer `buf` if it exists; advances the running pointer."""
+    ptr, rsrc, offs, dst = (S_KP, S_KR, "koff", "kdst") if which == "k" else (S_VP, S_VR, "voff", "vdst")
+    A.e(f"s_add_u32 {sr(S_TMP)}, {sr(S_T)}, {ahead}")
+    A.e(f"s_cmp_lt_u32 {sr(S_TMP)}, %[nkt]")
+    A.e(f"s_cbranch_scc0 {lbl_skip}")
+    # rows valid = min(64, kv_lim - 64*(t+ahead)); bytes = rows * row_bytes
+    A.e(f"s_lshl_b32 {sr(S_ROWS)}, {sr(S_TMP)}, 6")
+    A.e(f"s_sub_i32 {sr(S_ROWS)}, %[kvlim], {sr(S_ROWS)}")
+    A.e(f"s_min_i32 {sr(S_ROWS)}, {sr(S_ROWS)}, 64")
+    A.e(f"s_mul_i32 {sr(rsrc + 2)}, {sr(S_ROWS)}, %[rowb]")
+    A.e(f"s_mov_b32 {sr(rsrc)}, {sr(ptr)}")
+    A.e(f"s_and_b32 {sr(rsrc + 1)}, {sr(ptr + 1)}, 0xffff")
+    A.e(f"s_mov_b32 {sr(rsrc + 3)}, 0x20000")
+    A.e(f"s_add_u32 {sr(S_TMP)}, %[{dst}0], {buf * TILE_BYTES}")
+    for u in range(4):
+        A.e(f"s_mov_b32 m0, {sr(S_TMP)}")
+        A.e("s_nop 0")
+        A.e(f"buffer_load_dwordx4 %[{offs}{u}], {sr(rsrc, 4)}, 0 offen lds")
+        if u < 3:
+            A.e(f"s_add_u32 {sr(S_TMP)}, {sr(S_TMP)}, 1024")
+    # advance the running pointer by one tile
+    A.e(f"s_add_u32 {sr(ptr)}, {sr(ptr)}, %[tstride_lo]")
+    A.e(f"s_addc_u32 {sr(ptr + 1)}, {sr(ptr + 1)}, %[tstride_hi]")
+    A.e(f"{lbl_skip}:")
+
+
+def half(A, parity, uid):
+    """Process tile t (= S_T) whose S lives in set A (parity 0) or B (parity 1)."""
+    cur_base, nxt_base = (SA_BASE, SB_BASE) if parity == 0 else (SB_BASE, SA_BASE)
+    kb_read = 1 - parity       # K buffer holding tile t+1
+    vb_read = parity           # V buffer holding tile t
+    p = f"{parity}_{uid}"
+    dma(A, "k", parity, f"Lnok{p}", 2)           # K(t+2) -> K buffer t&1
+    dma(A, "v", 1 - parity, f"Lnov{p}", 1)       # V(t+1) -> V buffer (t+1)&1
+    A.e(f"s_add_u32 {sr(S_T1)}, {sr(S_T)}, 1")
+    A.e(f"s_cmp_lt_u32 {sr(S_T1)}, %[nkt]")
+    A.e(f"s_cbranch_scc0 Llast{p}")
+    A.e(f"s_lshl_b32 {sr(S_KEY)}, {sr(S_T1)}, 6")
+    A.e(f"s_cmp_ge_u32 {sr(S_T1)}, %[tmask]")
+    A.e(f"s_cbranch_scc1 Lmask{p}")
+    block(A, cur_base, nxt_base, kb_read, vb_read, True, False)
+    A.e(f"s_branch Lpost{p}")
+    A.e(f"Lmask{p}:")
+    block(A, cur_base, nxt_base, kb_read, vb_read, True, True)
+    A.e(f"Lpost{p}:")
+    rescale(A, f"Lnorescale{p}")
+    A.e("s_waitcnt vmcnt(0)")
+    A.e("s_barrier")
+    A.e(f"s_add_u32 {sr(S_T)}, {sr(S_T)}, 1")
+
+
+def last(A, parity, uid):
+    cur_base, nxt_base = (SA_BASE, SB_BASE) if parity == 0 else (SB_BASE, SA_BASE)
+    A.e(f"Llast{parity}_{uid}:")
+    block(A, cur_base, nxt_base, 1 - parity, parity, False, False)
+    A.e(f"s_branch Lend_{uid}")
+
+
+def gen_loop():
+    A = Asm()
+    uid = "%="
+    # running tile pointers: K starts at tile 2 (tiles 0, 1 are loaded before the loop), V at tile 1
+    A.e(f"s_mov_b32 {sr(S_T)}, 0")
+    A.e(f"s_mov_b32 {sr(S_KP)}, %[kp_lo]")
+    A.e(f"s_mov_b32 {sr(S_KP + 1)}, %[kp_hi]")
+    A.e(f"s_mov_b32 {sr(S_VP)}, %[vp_lo]")
+    A.e(f"s_mov_b32 {sr(S_VP + 1)}, %[vp_hi]")
+    A.e(f"s_cmp_lt_u32 {sr(S_T)}, %[nkt]")
+    A.e(f"s_cbranch_scc0 Lend_{uid}")
+    A.e(f"Ltop_{uid}:")
+    half(A, 0, uid)
+    half(A, 1, uid)
+    A.e(f"s_cmp_lt_u32 {sr(S_T)}, %[nkt]")
+    A.e(f"s_cbranch_scc1 Ltop_{uid}")
+    A.e(f"s_branch Lend_{uid}")
+    last(A, 0, uid)
+    last(A, 1, uid)
+    A.e(f"Lend_{uid}:")
+    return A.lines
+
+
+# Registers the loop writes besides its own "+v" operands: pinned accumulator / score sets and
+# the clobber list.  No input operand may be allocated inside these.
+WRITTEN_VGPRS = set(range(27, 64)) | set(range(96, 160)) | set(range(192, 256))
+WRITTEN_SGPRS = set(range(80, 100))
+READ_WRITE_OPERANDS = ("mrun", "lrun", "nmc")
+
+
+def _regs(tok):
+    """'v5' -> ('v', {5}); 's[4:7]' -> ('s', {4..7}); anything else -> None."""
+    import re
+    m = re.fullmatch(r"-?([vs])(\d+)", tok) or re.fullmatch(r"-?([vs])\[(\d+):(\d+)\]", tok)
+    if not m:
+        return None
+    lo = int(m.group(2))
+    hi = int(m.group(3)) if m.lastindex == 3 else lo
+    return m.group(1), set(range(lo, hi + 1))
+
+
+def check_operand_allocation(compiled_asm: str) -> dict:
+    """Matches every instance of the loop in compiler output (the text between ASMSTART and
+    ASMEND that starts like the loop) against the template, and checks that each named operand
+    got one register, that no two operands share one (read-write operands with anything) and that
+    no operand lies in a register the loop writes.  Returns {operand: register} of the last
+    instance; raises AssertionError on a violation."""
+    import re
+    tpl = gen_loop()
+    blocks = re.findall(r";;#ASMSTART\n(.*?);;#ASMEND", compiled_asm, flags=re.S)
+    loops = [b for b in blocks if b.lstrip().startswith(tpl[0].split()[0] + " s80, 0")]
+    assert loops, "loop statement not found in the compiled assembly"
+    result = {}
+    for body in loops:
+        got = [l.strip() for l in body.strip().splitlines() if l.strip()]
+        assert len(got) == len(tpl), (len(got), len(tpl))
+        names = {}
+        for t, g in zip(tpl, got):
+            pat, keys = "", []
+            for part in re.split(r"(%\[\w+\]|%=)", t):
+                if part == "%=":
+                    pat += r"\d+"
+                elif part.startswith("%["):
+                    keys.append(part[2:-1])
+                    pat += r"(\S+?)"
+                else:
+                    pat += re.escape(part)
+            m = re.fullmatch(pat, g.split(" ;")[0].rstrip(","))
+            assert m, f"compiled line does not match template: {g!r} vs {t!r}"
+            for k, v in zip(keys, m.groups()):
+                v = v.lstrip("-")
+                assert names.setdefault(k, v) == v, f"operand {k} in two registers: {names[k]}, {v}"
+        owner = {}
+        for k, v in names.items():
+            r = _regs(v)
+            if r is None:
+                continue  # literal or special operand
+            kind, regs = r
+            written = WRITTEN_VGPRS if kind == "v" else WRITTEN_SGPRS
+            assert not (regs & written), f"operand {k} = {v} lies in a register the loop writes"
+            for x in regs:
+                other = owner.setdefault((kind, x), k)
+                if other != k and (k in READ_WRITE_OPERANDS or other in READ_WRITE_OPERANDS):
+                    raise AssertionError(f"read-write operand shares {kind}{x}: {k}, {other}")
+        result = names
+    return result
+
+
+def main(out):
+    lines = gen_loop()
+    vclob = [f"v{i}" for i in range(V_BASE, V_BASE + 32)] + [f"v{i}" for i in (RS, MX, NEGINF, T0, ALPHA)]
+    sclob = [f"s{i}" for i in range(80, 100)]
+    clob = ", ".join('"%s"' % c for c in vclob + sclob + ["vcc", "scc", "m0", "memory"])
+    body = "".join('      "%s\\n\\t" \\\n' % l for l in lines)
+    txt = ("// Generated by gen_attn_loop.py (do not edit): main loop of the pipelined bf16 attention kernel.\n"
+           "#define THA_ATTN_LOOP_ASM \\\n" + body + "\n"
+           "#define THA_ATTN_LOOP_CLOBBERS " + clob + "\n")
+    open(out, "w").write(txt)
+
+
+if __name__ == "__main__":
+    import os
+    main(sys.argv[1] if len(sys.argv) > 1 else os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                            "attn_loop_d128.inc"))

@@ -39,5 +39,6 @@ hipError_t launch_merge_lse(int n_parts, const PartPtrs& parts, int part_dt, voi
                             int B, int S, int H, int D, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_bf16_d128(const AttnArgs& a, hipStream_t stream);
 
 }  // namespace tha
