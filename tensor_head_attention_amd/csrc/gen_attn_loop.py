@@ -12,17 +12,20 @@ Per 64-key tile t, for a wavefront of 32 query rows (the kernel source explains 
 Fragments are read from LDS three MFMAs ahead; each wait covers exactly the fragment needed.
 
 Register map (physical VGPRs, pinned by the operand constraints):
-  O^T[db]   v[192+16db : 207+16db]      (fp32 accumulators, 4 blocks of 32 dims)
+  O^T[db]   a[16db : 16db+15]           (fp32 accumulators in AGPRs, 4 blocks of 32 dims)
   S set A   v[128:159], S set B v[96:127] (scores of the current / next tile, alternating)
   Q^T[t]    v[64+4t : 67+4t]            (bf16 fragments, loaded once)
   K frags   v[48:63], V frags v[32:47]   (rotating prefetch buffers)
-  v31 row sum, v30 row max, v29 -inf, v28/v27 temporaries; s[80:99] scalar temporaries.
+  v31 row sum, v30 row max, v29 -inf, v28/v27 temporaries (the rescale also uses v[48:55]); s[80:99] scalar
+  temporaries.
 Wait states: every VALU read of an MFMA result, and every MFMA read of a VALU result, is separated
 from the writer by at least eight MFMAs or three s_nop 7, so no hazard needs hardware interlocks.
 """
 import sys
 
-O_BASE, SA_BASE, SB_BASE, Q_BASE, K_BASE, V_BASE = 192, 128, 96, 64, 48, 32
+SA_BASE, SB_BASE, Q_BASE, K_BASE, V_BASE = 128, 96, 64, 48, 32
+O_AGPR = 0                   # O^T accumulators in a[0:63]
+TMP_BASE, N_TMP = 48, 8      # rescale temporaries: the K fragment buffers, idle at that point
 RS, MX, NEGINF, T0, ALPHA = 31, 30, 29, 28, 27
 # scalar temporaries (clobbered)
 S_T, S_T1, S_KEY, S_ROWS, S_TMP = 80, 81, 82, 83, 84
@@ -33,6 +36,10 @@ TILE_BYTES = 16384
 
 def vr(a, n=1):
     return f"v{a}" if n == 1 else f"v[{a}:{a + n - 1}]"
+
+
+def ar(a, n=1):
+    return f"a{a}" if n == 1 else f"a[{a}:{a + n - 1}]"
 
 
 def sr(a, n=1):
@@ -153,8 +160,8 @@ def block(A, cur_base, nxt_base, kbuf, vbuf, has_next, mask_next):
         ks, db = divmod(i, 4)
         kb, h = divmod(ks, 2)
         A.wait_for(v_ops[i])
-        A.e(f"v_mfma_f32_32x32x16_bf16 {vr(O_BASE + 16 * db, 16)}, {vr(V_BASE + 4 * (i % 4), 4)}, "
-            f"{vr(cur(kb, 8 * h), 4)}, {vr(O_BASE + 16 * db, 16)}")
+        A.e(f"v_mfma_f32_32x32x16_bf16 {ar(O_AGPR + 16 * db, 16)}, {vr(V_BASE + 4 * (i % 4), 4)}, "
+            f"{vr(cur(kb, 8 * h), 4)}, {ar(O_AGPR + 16 * db, 16)}")
         for op in bsl[i]:
             A.e(op)
 
@@ -186,8 +193,14 @@ def rescale(A, lbl):
     A.e(f"v_cndmask_b32_e64 {vr(ALPHA)}, 1.0, {vr(ALPHA)}, vcc")      # lanes that keep their max: 1
     A.e(f"v_mov_b32 %[mrun], {vr(T0)}")
     A.e(f"v_mul_f32_e32 %[lrun], %[lrun], {vr(ALPHA)}")
-    for r in range(64):
-        A.e(f"v_mul_f32_e32 {vr(O_BASE + r)}, {vr(O_BASE + r)}, {vr(ALPHA)}")
+    # O^T lives in AGPRs: read 8 at a time into temporaries, scale, write back
+    for g in range(0, 64, N_TMP):
+        for j in range(N_TMP):
+            A.e(f"v_accvgpr_read_b32 {vr(TMP_BASE + j)}, {ar(O_AGPR + g + j)}")
+        for j in range(N_TMP):
+            A.e(f"v_mul_f32_e32 {vr(TMP_BASE + j)}, {vr(TMP_BASE + j)}, {vr(ALPHA)}")
+        for j in range(N_TMP):
+            A.e(f"v_accvgpr_write_b32 {ar(O_AGPR + g + j)}, {vr(TMP_BASE + j)}")
     A.e("s_nop 1")
     A.e(f"{lbl}:")
     A.e(f"v_mul_f32_e64 %[nmc], -%[mrun], %[c]")
@@ -279,15 +292,16 @@ def gen_loop():
 
 # Registers the loop writes besides its own "+v" operands: pinned accumulator / score sets and
 # the clobber list.  No input operand may be allocated inside these.
-WRITTEN_VGPRS = set(range(27, 64)) | set(range(96, 160)) | set(range(192, 256))
+WRITTEN_VGPRS = set(range(27, 64)) | set(range(96, 160)) | set(range(TMP_BASE, TMP_BASE + N_TMP))
 WRITTEN_SGPRS = set(range(80, 100))
+WRITTEN_AGPRS = set(range(O_AGPR, O_AGPR + 64))
 READ_WRITE_OPERANDS = ("mrun", "lrun", "nmc")
 
 
 def _regs(tok):
-    """'v5' -> ('v', {5}); 's[4:7]' -> ('s', {4..7}); anything else -> None."""
+    """'v5' -> ('v', {5}); 's[4:7]' -> ('s', {4..7}); 'a3' -> ('a', {3}); anything else -> None."""
     import re
-    m = re.fullmatch(r"-?([vs])(\d+)", tok) or re.fullmatch(r"-?([vs])\[(\d+):(\d+)\]", tok)
+    m = re.fullmatch(r"-?([vsa])(\d+)", tok) or re.fullmatch(r"-?([vsa])\[(\d+):(\d+)\]", tok)
     if not m:
         return None
     lo = int(m.group(2))
@@ -332,7 +346,7 @@ def check_operand_allocation(compiled_asm: str) -> dict:
             if r is None:
                 continue  # literal or special operand
             kind, regs = r
-            written = WRITTEN_VGPRS if kind == "v" else WRITTEN_SGPRS
+            written = {"v": WRITTEN_VGPRS, "s": WRITTEN_SGPRS, "a": WRITTEN_AGPRS}[kind]
             assert not (regs & written), f"operand {k} = {v} lies in a register the loop writes"
             for x in regs:
                 other = owner.setdefault((kind, x), k)
@@ -345,6 +359,7 @@ def check_operand_allocation(compiled_asm: str) -> dict:
 def main(out):
     lines = gen_loop()
     vclob = [f"v{i}" for i in range(V_BASE, V_BASE + 32)] + [f"v{i}" for i in (RS, MX, NEGINF, T0, ALPHA)]
+    vclob += [f"v{i}" for i in range(TMP_BASE, TMP_BASE + N_TMP)]
     sclob = [f"s{i}" for i in range(80, 100)]
     clob = ", ".join('"%s"' % c for c in vclob + sclob + ["vcc", "scc", "m0", "memory"])
     body = "".join('      "%s\\n\\t" \\\n' % l for l in lines)
