@@ -92,6 +92,10 @@ enum {
  * section 3.2 casts the fp32 softmax back to the input type);
  * in_dt = THA_F32 with 1 <= D <= 256 (fp32 throughout).  out_dt may be THA_BF16
  * or THA_F32 in both cases (fp32 output keeps ring partials unrounded).
+ * Kernel choice for bf16, D = 128: a wide kernel (256 query rows per workgroup)
+ * when its grid holds at least two workgroups per compute unit, else a narrow one
+ * (128 rows); both compute the same function.  The environment variable
+ * THA_ATTN_D128_KERNEL=narrow|wide, read on every call, forces one of them.
  * Errors: THA_ERR_INVALID for null q/k/v/o, non-positive sizes, unknown mask
  * bits, KEY_PADDING without kv_len, scale not finite and positive, |q_pos0| or |k_pos0| >=
  * 2^62; THA_ERR_UNSUPPORTED for other dtypes / head dims.

@@ -42,10 +42,11 @@ def _compile(src: str) -> str:
 
 
 def generate_sources() -> None:
-    """Regenerate the hand-scheduled attention loop (attn_loop_d128.inc) from its generator."""
-    r = subprocess.run([sys.executable, os.path.join(CSRC, "gen_attn_loop.py")], capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"gen_attn_loop.py failed:\n{r.stdout}{r.stderr}")
+    """Regenerate the hand-scheduled attention loops (attn_loop_d128*.inc) from their generators."""
+    for gen in ("gen_attn_loop.py", "gen_attn_loop_wide.py"):
+        r = subprocess.run([sys.executable, os.path.join(CSRC, gen)], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"{gen} failed:\n{r.stdout}{r.stderr}")
 
 
 def build_library(jobs: int = 8) -> str:

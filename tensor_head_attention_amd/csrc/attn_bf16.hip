@@ -39,6 +39,9 @@
 //  * Heaviest causal query tiles are launched first; consecutive workgroups
 //    take different heads of one query tile, so each head's workgroups land on
 //    one XCD (dispatch is round-robin over the 8 XCDs) and share its L2.
+#include <cstdlib>
+#include <cstring>
+
 #include "device_common.h"
 #include "tha_kernels.h"
 
@@ -344,10 +347,28 @@ hipError_t launch_d(const AttnArgs& x, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Head size 128: the wide kernel (256 rows per workgroup, one workgroup per CU) when its grid
+// fills every CU at least twice, else the narrow one (128 rows, two workgroups per CU), which
+// keeps small grids spread over the chip.  THA_ATTN_D128_KERNEL=narrow|wide forces a choice.
+bool use_wide_d128(const AttnArgs& a) {
+  const char* force = getenv("THA_ATTN_D128_KERNEL");
+  if (force && strcmp(force, "wide") == 0) return true;
+  if (force && strcmp(force, "narrow") == 0) return false;
+  static int cu_count[64];  // per device, filled on first use
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  if (cu_count[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return false;
+    cu_count[dev] = n;
+  }
+  return attn_bf16_d128_wide_blocks(a) >= 2 * (int64_t)cu_count[dev];
+}
+
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
-  if (a.D == 128) return launch_attn_bf16_d128(a, st);  // software-pipelined kernel
+  if (a.D == 128) return use_wide_d128(a) ? launch_attn_bf16_d128_wide(a, st) : launch_attn_bf16_d128(a, st);
   if (a.D == 64) return launch_d<64>(a, st);
   return hipErrorInvalidValue;
 }

@@ -1,0 +1,446 @@
+#!/usr/bin/env python3
+"""Writes attn_loop_d128_wide.inc: the main loop of the wide bf16 attention kernel (head size 128,
+64 query rows per wavefront) as the text of one inline-asm statement, scheduled by hand for CDNA4
+(gfx950).  The build runs this script before compiling attn_bf16_d128_wide.hip, which defines the
+operands and the C++ around the loop.
+
+Per 64-key tile t, for a wavefront of 64 query rows (two 32-row blocks qb = 0, 1):
+  phase A: S(t+1) = K(t+1) Q^T, 32 v_mfma_f32_32x32x16_bf16 (each K fragment read from LDS feeds
+           the MFMAs of both row blocks), each followed by a slice of the softmax of tile t:
+           p = 2^(s*c + neg_mc) and the bf16 packing of P into its own registers;
+  phase B: O^T += V(t)^T P(t)^T, 32 MFMAs (each V fragment feeds both row blocks), each followed
+           by a slice of the row sums of tile t (fp32) and of the mask and row max of tile t+1;
+  then the lazy running-max update and the barrier.
+K and V tiles are triple buffered in LDS: the copies of K(t+3) and V(t+2) are issued at the start
+of block t, and the first K fragments of the next block are read before the barrier that ends this
+one, so no LDS read ever waits behind a barrier.  Fragment reads run three fragments (six MFMAs)
+ahead; each wait covers exactly the fragment needed.
+
+Register map (pinned by the operand constraints):
+  O^T[qb][db]  a[64qb + 16db : +15]       fp32 accumulators (AGPRs)
+  Q^T[qb][tt]  a[128 + 32qb + 4tt : +3]   bf16 B operands of the score product (AGPRs)
+  S sets       v[128:191] (A), v[192:255] (B); S[qb][kb] at base + 32qb + 16kb
+  K frags      v[96:111], V frags v[112:127] (4 rotating fragments each)
+  P[qb][ks]    v[64 + 16qb + 4ks : +3]    bf16 probabilities of the current tile
+  v[54:63]     row max / mask bound / alpha / row sum per row block, -inf, a temporary
+  s[80:99]     scalar temporaries
+Wait states: VALU reads of MFMA results and MFMA reads of VALU results are separated by at least
+two MFMAs; before O^T is read by VALU the loop issues three s_nop 7.
+"""
+import os
+import re
+import sys
+
+# ---- registers ----
+A_O, A_Q = 0, 128
+V_SA, V_SB = 128, 192
+V_KF, V_VF, V_P = 96, 112, 64
+V_MX = (62, 63)
+V_T0 = (60, 61)
+V_AL = (58, 59)
+V_RS = (56, 57)
+V_NEGINF = 55
+V_TMP = 54
+TMP_BASE, N_TMP = V_VF, 8   # rescale temporaries: the V fragment buffers, idle at that point
+
+S_T, S_T1, S_KEY, S_ROWS, S_TMP, S_X = 80, 81, 82, 83, 84, 85
+S_KP, S_VP = 86, 88          # running 64-bit K / V tile pointers
+S_B0, S_Y = 90, 91           # S_B0 = t mod 3
+S_KR, S_VR = 92, 96          # buffer resource quads
+TILE_BYTES = 16384
+NBUF = 3
+
+
+def vr(a, n=1):
+    return f"v{a}" if n == 1 else f"v[{a}:{a + n - 1}]"
+
+
+def ar(a, n=1):
+    return f"a{a}" if n == 1 else f"a[{a}:{a + n - 1}]"
+
+
+def sr(a, n=1):
+    return f"s{a}" if n == 1 else f"s[{a}:{a + n - 1}]"
+
+
+class Asm:
+    def __init__(self):
+        self.lines = []
+        self.n_ops = 0  # LDS ops issued in the current block (including those in flight at entry)
+
+    def e(self, s):
+        self.lines.append(s)
+
+    def lds(self, s):
+        self.e(s)
+        self.n_ops += 1
+        return self.n_ops - 1
+
+    def wait_for(self, op):
+        n = max(0, min(self.n_ops - 1 - op, 15))
+        self.e(f"s_waitcnt lgkmcnt({n})")
+
+
+def s_reg(base, qb, kb, r=0):
+    return base + 32 * qb + 16 * kb + r
+
+
+def issue_k(A, i):
+    """K fragment i (kb = i // 8, dims 16tt..: tt = i % 8) of the tile ka points at."""
+    kb, tt = divmod(i, 8)
+    return A.lds(f"ds_read_b128 {vr(V_KF + 4 * (i % 4), 4)}, %[ka{tt}] offset:{kb * 8192}")
+
+
+def issue_v(A, j):
+    """V fragment j (16-key step ks = j // 4, 32-dim block db = j % 4) of the tile va points at."""
+    ks, db = divmod(j, 4)
+    base = V_VF + 4 * (j % 4)
+    A.lds(f"ds_read_b64_tr_b16 {vr(base, 2)}, %[va{db}] offset:{ks * 4096}")
+    return A.lds(f"ds_read_b64_tr_b16 {vr(base + 2, 2)}, %[va{db}] offset:{ks * 4096 + 2048}")
+
+
+def block(A, cur, nxt, has_next, masked):
+    """One tile.  With has_next, K fragments 0..2 of tile t+1 are in flight at entry."""
+    A.n_ops = 0
+    k_ops, v_ops = {}, {}
+    if has_next:
+        for i in range(3):
+            k_ops[i] = i
+        A.n_ops = 3
+    else:
+        A.e("s_waitcnt lgkmcnt(0)")
+    if masked:
+        A.e(f"v_mov_b32 {vr(V_NEGINF)}, 0xff800000")
+        for qb in range(2):  # hide in-tile key c (without its 4hi part) when c >= base2 - key0
+            A.e(f"v_subrev_u32_e32 {vr(V_T0[qb])}, {sr(S_KEY)}, %[base2_{qb}]")
+
+    # softmax pairs of S(t), in the order the value product consumes P: pair s -> (ks, qb, m)
+    pairs = []
+    for ks in range(4):
+        kb, h = divmod(ks, 2)
+        for qb in range(2):
+            for m in range(4):
+                a = s_reg(cur, qb, kb, 8 * h + 2 * m)
+                pairs.append((qb, ks, m, a, a + 1))
+
+    def cvt(p):
+        qb, ks, m, a, b = pairs[p]
+        return f"v_cvt_pk_bf16_f32 {vr(V_P + 16 * qb + 4 * ks + m)}, {vr(a)}, {vr(b)}"
+
+    slots_a = []
+    for p, (qb, ks, m, a, b) in enumerate(pairs):
+        ops = [f"v_fma_f32 {vr(a)}, {vr(a)}, %[c], %[nmc{qb}]",
+               f"v_fma_f32 {vr(b)}, {vr(b)}, %[c], %[nmc{qb}]",
+               f"v_exp_f32_e32 {vr(a)}, {vr(a)}",
+               f"v_exp_f32_e32 {vr(b)}, {vr(b)}"]
+        if p > 0:
+            ops.append(cvt(p - 1))  # the previous pair: its exp results are a slot old
+        slots_a.append(ops)
+
+    # ---- phase A ----
+    if has_next:
+        for s in range(32):
+            i, qb = divmod(s, 2)
+            kb, tt = divmod(i, 8)
+            if qb == 0:
+                if i + 3 < 16:
+                    k_ops[i + 3] = issue_k(A, i + 3)
+                else:
+                    jv = i + 3 - 16
+                    v_ops[jv] = issue_v(A, jv)
+                A.wait_for(k_ops[i])
+            dst = s_reg(nxt, qb, kb)
+            src2 = "0" if tt == 0 else vr(dst, 16)
+            A.e(f"v_mfma_f32_32x32x16_bf16 {vr(dst, 16)}, {vr(V_KF + 4 * (i % 4), 4)}, "
+                f"{ar(A_Q + 32 * qb + 4 * tt, 4)}, {src2}")
+            for op in slots_a[s]:
+                A.e(op)
+    else:
+        for jv in range(3):
+            v_ops[jv] = issue_v(A, jv)
+        for s in range(32):
+            for op in slots_a[s]:
+                A.e(op)
+
+    # ---- phase B ----
+    slots_b = [[] for _ in range(32)]
+    for p, (qb, ks, m, a, b) in enumerate(pairs):  # row sums of S(t) (fp32 probabilities)
+        slots_b[p] += [f"v_add_f32_e32 {vr(V_RS[qb])}, {vr(V_RS[qb])}, {vr(a)}",
+                       f"v_add_f32_e32 {vr(V_RS[qb])}, {vr(V_RS[qb])}, {vr(b)}"]
+    if has_next:  # mask and row max of S(t+1): (qb, kb) blocks in the order their MFMAs finished
+        order = [(0, 0), (1, 0), (0, 1), (1, 1)]
+        first = {0: True, 1: True}
+        for bi, (qb, kb) in enumerate(order):
+            for r2 in range(8):
+                s = bi * 8 + r2
+                ea = s_reg(nxt, qb, kb, 2 * r2)
+                eb = ea + 1
+                if masked:
+                    for r, e_ in ((2 * r2, ea), (2 * r2 + 1, eb)):
+                        cconst = kb * 32 + (r >> 2) * 8 + (r & 3)
+                        slots_b[s].append(f"v_cmp_ge_i32_e32 vcc, {cconst}, {vr(V_T0[qb])}")
+                        slots_b[s].append(f"v_cndmask_b32_e32 {vr(e_)}, {vr(e_)}, {vr(V_NEGINF)}, vcc")
+                if first[qb]:
+                    slots_b[s].append(f"v_max_f32_e32 {vr(V_MX[qb])}, {vr(ea)}, {vr(eb)}")
+                    first[qb] = False
+                else:
+                    slots_b[s].append(f"v_max3_f32 {vr(V_MX[qb])}, {vr(V_MX[qb])}, {vr(ea)}, {vr(eb)}")
+
+    A.e(f"v_mov_b32 {vr(V_RS[0])}, 0")
+    A.e(f"v_mov_b32 {vr(V_RS[1])}, 0")
+    for s in range(32):
+        j, qb = divmod(s, 2)
+        ks, db = divmod(j, 4)
+        if qb == 0:
+            if j + 3 < 16:
+                v_ops[j + 3] = issue_v(A, j + 3)
+            A.wait_for(v_ops[j])
+        A.e(f"v_mfma_f32_32x32x16_bf16 {ar(A_O + 64 * qb + 16 * db, 16)}, {vr(V_VF + 4 * (j % 4), 4)}, "
+            f"{vr(V_P + 16 * qb + 4 * ks, 4)}, {ar(A_O + 64 * qb + 16 * db, 16)}")
+        if s == 0:
+            A.e(cvt(31))  # last pair of P (read by the MFMAs of step ks = 3)
+        for op in slots_b[s]:
+            A.e(op)
+
+    if has_next:
+        A.e("s_nop 1")
+        for qb in range(2):
+            A.e(f"v_mov_b32 {vr(V_AL[qb])}, {vr(V_MX[qb])}")
+        A.e("s_nop 1")
+        for qb in range(2):
+            A.e(f"v_permlane32_swap_b32_e32 {vr(V_AL[qb])}, {vr(V_MX[qb])}")
+        A.e("s_nop 1")
+        for qb in range(2):
+            A.e(f"v_max_f32_e32 {vr(V_MX[qb])}, {vr(V_AL[qb])}, {vr(V_MX[qb])}")
+    for qb in range(2):
+        A.e(f"v_add_f32_e32 %[lrun{qb}], %[lrun{qb}], {vr(V_RS[qb])}")
+    # O^T (MFMA results) may be read by VALU next: keep >= 24 wait states
+    A.e("s_nop 7")
+    A.e("s_nop 7")
+    A.e("s_nop 7")
+
+
+def rescale(A, qb, lbl):
+    """Lazy running-max update of row block qb from its next-tile max, then its neg_mc."""
+    t0, al, mx = V_T0[qb], V_AL[qb], V_MX[qb]
+    A.e(f"v_add_f32_e32 {vr(t0)}, %[thr], %[mrun{qb}]")
+    A.e(f"v_cmp_gt_f32_e32 vcc, {vr(mx)}, {vr(t0)}")
+    A.e("s_nop 4")                                                        # VALU vcc -> vccz branch
+    A.e(f"s_cbranch_vccz {lbl}")
+    A.e(f"v_cndmask_b32_e32 {vr(t0)}, %[mrun{qb}], {vr(mx)}, vcc")     # m_new
+    A.e(f"v_sub_f32_e32 {vr(al)}, %[mrun{qb}], {vr(t0)}")
+    A.e(f"v_mul_f32_e32 {vr(al)}, %[c], {vr(al)}")
+    A.e(f"v_exp_f32_e32 {vr(al)}, {vr(al)}")
+    A.e("s_nop 0")                                                        # transcendental -> VALU
+    A.e(f"v_cndmask_b32_e64 {vr(al)}, 1.0, {vr(al)}, vcc")             # rows that keep their max: 1
+    A.e(f"v_mov_b32 %[mrun{qb}], {vr(t0)}")
+    A.e(f"v_mul_f32_e32 %[lrun{qb}], %[lrun{qb}], {vr(al)}")
+    base = A_O + 64 * qb
+    for g in range(0, 64, N_TMP):
+        for j in range(N_TMP):
+            A.e(f"v_accvgpr_read_b32 {vr(TMP_BASE + j)}, {ar(base + g + j)}")
+        for j in range(N_TMP):
+            A.e(f"v_mul_f32_e32 {vr(TMP_BASE + j)}, {vr(TMP_BASE + j)}, {vr(al)}")
+        for j in range(N_TMP):
+            A.e(f"v_accvgpr_write_b32 {ar(base + g + j)}, {vr(TMP_BASE + j)}")
+    A.e("s_nop 1")
+    A.e(f"{lbl}:")
+    A.e(f"v_mul_f32_e64 %[nmc{qb}], -%[mrun{qb}], %[c]")
+    A.e(f"v_cmp_eq_f32_e32 vcc, 0xff800000, %[mrun{qb}]")
+    A.e(f"v_cndmask_b32_e64 %[nmc{qb}], %[nmc{qb}], 0, vcc")
+
+
+def buf_index(A, dst, add):
+    """dst = (S_B0 + add) mod 3."""
+    if add == 0:
+        A.e(f"s_mov_b32 {sr(dst)}, {sr(S_B0)}")
+        return
+    A.e(f"s_add_u32 {sr(dst)}, {sr(S_B0)}, {add}")
+    A.e(f"s_sub_u32 {sr(S_Y)}, {sr(dst)}, {NBUF}")
+    A.e(f"s_cmp_ge_u32 {sr(dst)}, {NBUF}")
+    A.e(f"s_cselect_b32 {sr(dst)}, {sr(S_Y)}, {sr(dst)}")
+
+
+def dma(A, which, lbl_skip, ahead, buf_add):
+    """Copy tile t + ahead of K or V into LDS buffer (t + buf_add) mod 3 if it exists."""
+    ptr, rsrc, offs, dst = (S_KP, S_KR, "koff", "kdst") if which == "k" else (S_VP, S_VR, "voff", "vdst")
+    A.e(f"s_add_u32 {sr(S_TMP)}, {sr(S_T)}, {ahead}")
+    A.e(f"s_cmp_lt_u32 {sr(S_TMP)}, %[nkt]")
+    A.e(f"s_cbranch_scc0 {lbl_skip}")
+    A.e(f"s_lshl_b32 {sr(S_ROWS)}, {sr(S_TMP)}, 6")           # rows = min(64, kv_lim - 64 (t + ahead))
+    A.e(f"s_sub_i32 {sr(S_ROWS)}, %[kvlim], {sr(S_ROWS)}")
+    A.e(f"s_min_i32 {sr(S_ROWS)}, {sr(S_ROWS)}, 64")
+    A.e(f"s_mul_i32 {sr(rsrc + 2)}, {sr(S_ROWS)}, %[rowb]")
+    A.e(f"s_mov_b32 {sr(rsrc)}, {sr(ptr)}")
+    A.e(f"s_and_b32 {sr(rsrc + 1)}, {sr(ptr + 1)}, 0xffff")
+    A.e(f"s_mov_b32 {sr(rsrc + 3)}, 0x20000")
+    buf_index(A, S_X, buf_add)
+    A.e(f"s_lshl_b32 {sr(S_X)}, {sr(S_X)}, 14")
+    A.e(f"s_add_u32 {sr(S_TMP)}, %[{dst}0], {sr(S_X)}")
+    for u in range(4):
+        A.e(f"s_mov_b32 m0, {sr(S_TMP)}")
+        A.e("s_nop 0")
+        A.e(f"buffer_load_dwordx4 %[{offs}{u}], {sr(rsrc, 4)}, 0 offen lds")
+        if u < 3:
+            A.e(f"s_add_u32 {sr(S_TMP)}, {sr(S_TMP)}, 1024")
+    A.e(f"s_add_u32 {sr(ptr)}, {sr(ptr)}, %[tstride_lo]")
+    A.e(f"s_addc_u32 {sr(ptr + 1)}, {sr(ptr + 1)}, %[tstride_hi]")
+    A.e(f"{lbl_skip}:")
+
+
+def rotate(A, names, wrap_when):
+    """Move LDS read addresses to the next buffer: +16 KiB, or back from buffer 2 to 0 when
+    S_B0 == wrap_when."""
+    A.e(f"s_mov_b32 {sr(S_X)}, 0x4000")                        # +16 KiB
+    A.e(f"s_mov_b32 {sr(S_Y)}, 0xffff8000")                    # -32 KiB
+    A.e(f"s_cmp_eq_u32 {sr(S_B0)}, {wrap_when}")
+    A.e(f"s_cselect_b32 {sr(S_X)}, {sr(S_Y)}, {sr(S_X)}")
+    for n in names:
+        A.e(f"v_add_u32_e32 %[{n}], {sr(S_X)}, %[{n}]")
+
+
+KA = [f"ka{t}" for t in range(8)]
+VA = [f"va{d}" for d in range(4)]
+
+
+def half(A, parity, uid):
+    cur, nxt = (V_SA, V_SB) if parity == 0 else (V_SB, V_SA)
+    p = f"{parity}_{uid}"
+    dma(A, "k", f"Lnok{p}", 3, 0)        # K(t+3) -> buffer t mod 3 (held K(t), consumed)
+    dma(A, "v", f"Lnov{p}", 2, 2)        # V(t+2) -> buffer (t+2) mod 3 (held V(t-1), consumed)
+    rotate(A, VA, 0)                      # va: buffer (t-1) mod 3 -> t mod 3
+    A.e(f"s_add_u32 {sr(S_T1)}, {sr(S_T)}, 1")
+    A.e(f"s_cmp_lt_u32 {sr(S_T1)}, %[nkt]")
+    A.e(f"s_cbranch_scc0 Llast{p}")
+    A.e(f"s_lshl_b32 {sr(S_KEY)}, {sr(S_T1)}, 6")
+    A.e(f"s_cmp_ge_u32 {sr(S_T1)}, %[tmask]")
+    A.e(f"s_cbranch_scc1 Lmask{p}")
+    block(A, cur, nxt, True, False)
+    A.e(f"s_branch Lpost{p}")
+    A.e(f"Lmask{p}:")
+    block(A, cur, nxt, True, True)
+    A.e(f"Lpost{p}:")
+    rescale(A, 0, f"Lnor0_{p}")
+    rescale(A, 1, f"Lnor1_{p}")
+    rotate(A, KA, 1)                      # ka: buffer (t+1) mod 3 -> (t+2) mod 3
+    A.e(f"s_add_u32 {sr(S_TMP)}, {sr(S_T)}, 2")
+    A.e(f"s_cmp_lt_u32 {sr(S_TMP)}, %[nkt]")
+    A.e(f"s_cbranch_scc0 Lnopre{p}")
+    for i in range(3):                    # first K fragments of the next block (K(t+2) is visible)
+        issue_k(A, i)
+    A.e(f"Lnopre{p}:")
+    A.e("s_waitcnt vmcnt(0)")
+    A.e("s_barrier")
+    A.e(f"s_add_u32 {sr(S_T)}, {sr(S_T)}, 1")
+    buf_index(A, S_B0, 1)
+
+
+def last(A, parity, uid):
+    cur, nxt = (V_SA, V_SB) if parity == 0 else (V_SB, V_SA)
+    A.e(f"Llast{parity}_{uid}:")
+    block(A, cur, nxt, False, False)
+    A.e(f"s_branch Lend_{uid}")
+
+
+def gen_loop():
+    A = Asm()
+    uid = "%="
+    A.e(f"s_mov_b32 {sr(S_T)}, 0")
+    A.e(f"s_mov_b32 {sr(S_B0)}, 0")
+    A.e(f"s_mov_b32 {sr(S_KP)}, %[kp_lo]")
+    A.e(f"s_mov_b32 {sr(S_KP + 1)}, %[kp_hi]")
+    A.e(f"s_mov_b32 {sr(S_VP)}, %[vp_lo]")
+    A.e(f"s_mov_b32 {sr(S_VP + 1)}, %[vp_hi]")
+    A.e(f"s_cmp_lt_u32 {sr(S_T)}, %[nkt]")
+    A.e(f"s_cbranch_scc0 Lend_{uid}")
+    A.e("s_cmp_lt_u32 1, %[nkt]")
+    A.e(f"s_cbranch_scc0 Ltop_{uid}")
+    for i in range(3):                    # first K fragments of tile 1 (ka points at buffer 1)
+        issue_k(A, i)
+    A.e(f"Ltop_{uid}:")
+    half(A, 0, uid)
+    half(A, 1, uid)
+    A.e(f"s_branch Ltop_{uid}")
+    last(A, 0, uid)
+    last(A, 1, uid)
+    A.e(f"Lend_{uid}:")
+    return A.lines
+
+
+VCLOB = list(range(V_P, 128)) + list(range(V_TMP, 64))
+SCLOB = list(range(80, 100))
+
+
+def main(out):
+    lines = gen_loop()
+    clob = ", ".join('"%s"' % c for c in [f"v{i}" for i in VCLOB] + [f"s{i}" for i in SCLOB]
+                     + ["vcc", "scc", "m0", "memory"])
+    body = "".join('      "%s\\n\\t" \\\n' % l for l in lines)
+    txt = ("// Generated by gen_attn_loop_wide.py (do not edit): main loop of the wide bf16 attention kernel.\n"
+           "#define THA_ATTN_WIDE_LOOP_ASM \\\n" + body + "\n"
+           "#define THA_ATTN_WIDE_LOOP_CLOBBERS " + clob + "\n")
+    open(out, "w").write(txt)
+
+
+# Registers the loop writes besides its own read-write operands (pinned sets and clobbers).
+WRITTEN = {"v": set(VCLOB) | set(range(V_SA, 256)), "s": set(SCLOB), "a": set(range(A_O, A_O + 128))}
+READ_WRITE_OPERANDS = tuple([f"mrun{q}" for q in range(2)] + [f"lrun{q}" for q in range(2)]
+                            + [f"nmc{q}" for q in range(2)] + KA + VA)
+
+
+def _regs(tok):
+    m = re.fullmatch(r"-?([vsa])(\d+)", tok) or re.fullmatch(r"-?([vsa])\[(\d+):(\d+)\]", tok)
+    if not m:
+        return None
+    lo = int(m.group(2))
+    hi = int(m.group(3)) if m.lastindex == 3 else lo
+    return m.group(1), set(range(lo, hi + 1))
+
+
+def check_operand_allocation(compiled_asm: str) -> dict:
+    """Matches each instance of the loop in compiler output against the template and checks that
+    every named operand got one register, that no read-write operand shares a register with
+    another operand, and that no operand lies in a register the loop writes.  Returns
+    {operand: register} of the last instance; raises AssertionError on a violation."""
+    tpl = gen_loop()
+    blocks = re.findall(r";;#ASMSTART\n(.*?);;#ASMEND", compiled_asm, flags=re.S)
+    loops = [b for b in blocks if [l.strip() for l in b.strip().splitlines()[:2]] == tpl[:2]]
+    assert loops, "loop statement not found in the compiled assembly"
+    result = {}
+    for body in loops:
+        got = [l.strip() for l in body.strip().splitlines() if l.strip()]
+        assert len(got) == len(tpl), (len(got), len(tpl))
+        names = {}
+        for t, g in zip(tpl, got):
+            pat, keys = "", []
+            for part in re.split(r"(%\[\w+\]|%=)", t):
+                if part == "%=":
+                    pat += r"\d+"
+                elif part.startswith("%["):
+                    keys.append(part[2:-1])
+                    pat += r"(\S+?)"
+                else:
+                    pat += re.escape(part)
+            m = re.fullmatch(pat, g.split(" ;")[0].rstrip(","))
+            assert m, f"compiled line does not match template: {g!r} vs {t!r}"
+            for k, v in zip(keys, m.groups()):
+                v = v.lstrip("-")
+                assert names.setdefault(k, v) == v, f"operand {k} in two registers: {names[k]}, {v}"
+        owner = {}
+        for k, v in names.items():
+            r = _regs(v)
+            if r is None:
+                continue
+            kind, regs = r
+            assert not (regs & WRITTEN[kind]), f"operand {k} = {v} lies in a register the loop writes"
+            for x in regs:
+                other = owner.setdefault((kind, x), k)
+                if other != k and (k in READ_WRITE_OPERANDS or other in READ_WRITE_OPERANDS):
+                    raise AssertionError(f"read-write operand shares {kind}{x}: {k}, {other}")
+        result = names
+    return result
+
+
+if __name__ == "__main__":
+    main(sys.argv[1] if len(sys.argv) > 1 else os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                            "attn_loop_d128_wide.inc"))

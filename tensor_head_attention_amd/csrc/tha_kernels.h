@@ -40,5 +40,7 @@ hipError_t launch_merge_lse(int n_parts, const PartPtrs& parts, int part_dt, voi
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_bf16_d128(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_bf16_d128_wide(const AttnArgs& a, hipStream_t stream);
+int64_t attn_bf16_d128_wide_blocks(const AttnArgs& a);
 
 }  // namespace tha

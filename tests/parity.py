@@ -6,6 +6,8 @@ Tolerances (per the workload definitions):
                 over the whole output, on the same bf16-rounded inputs; lse <= 1e-4
 A row with no visible key must give o = 0 and lse = -inf on both sides.
 """
+import contextlib
+import os
 import sys
 
 import torch
@@ -50,3 +52,21 @@ def check_lse(dev_lse: torch.Tensor, ref: torch.Tensor, in_dtype: torch.dtype, w
     if fin.any():
         err = (l[fin] - ref[fin]).abs().max().item()
         assert err <= TOL[in_dtype]["lse"], f"{what}: max-abs {err:.3e} > {TOL[in_dtype]['lse']}"
+
+
+@contextlib.contextmanager
+def d128_kernel(name):
+    """Force the bf16 head-size-128 attention kernel (narrow / wide; None = automatic choice)
+    for the calls inside, through the library's THA_ATTN_D128_KERNEL variable."""
+    old = os.environ.get("THA_ATTN_D128_KERNEL")
+    if name is None:
+        os.environ.pop("THA_ATTN_D128_KERNEL", None)
+    else:
+        os.environ["THA_ATTN_D128_KERNEL"] = name
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("THA_ATTN_D128_KERNEL", None)
+        else:
+            os.environ["THA_ATTN_D128_KERNEL"] = old

@@ -6,6 +6,7 @@ register the loop writes would be overwritten mid-loop.  These tests compile the
 gfx950 assembly and check the allocation, and check that the committed generated loop matches its
 generator."""
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -16,6 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "tensor_head_attention_amd", "csrc")
 sys.path.insert(0, CSRC)
 import gen_attn_loop as G  # noqa: E402
+import gen_attn_loop_wide as GW  # noqa: E402
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -55,4 +57,92 @@ def test_operand_registers_do_not_overlap_loop_writes(tmp_path):
                {"koff%d" % i for i in range(4)} | {"voff%d" % i for i in range(4)} | \
                {"mrun", "lrun", "nmc", "base2", "c", "thr", "nkt", "tmask", "kvlim", "rowb", "kp_lo", "kp_hi",
                 "vp_lo", "vp_hi", "tstride_lo", "tstride_hi", "kdst0", "vdst0"}
+    assert expected <= set(names), expected - set(names)
+
+
+def test_wide_generated_loop_is_current(tmp_path):
+    out = tmp_path / "loop.inc"
+    GW.main(str(out))
+    with open(os.path.join(CSRC, "attn_loop_d128_wide.inc")) as f:
+        assert f.read() == out.read_text(), "attn_loop_d128_wide.inc is stale: rerun gen_attn_loop_wide.py"
+
+
+def test_wide_loop_structure():
+    lines = GW.gen_loop()
+    # 64 MFMAs per tile with a successor (two parities x unmasked/masked), 32 per last tile
+    assert sum(l.startswith("v_mfma") for l in lines) == 2 * 2 * 64 + 2 * 32
+    for l in lines:
+        if "lgkmcnt(" in l:
+            assert 0 <= int(l.split("lgkmcnt(")[1].rstrip(")")) <= 15
+    assert sum(l == "s_barrier" for l in lines) == 2
+    # tile copies are only ever waited for as a whole, before a barrier
+    assert not any(l.startswith("s_waitcnt vmcnt(") and l != "s_waitcnt vmcnt(0)" for l in lines)
+
+
+def _regset(tok):
+    m = re.fullmatch(r"([va])\[(\d+):(\d+)\]", tok) or re.fullmatch(r"([va])(\d+)", tok)
+    lo = int(m.group(2))
+    hi = int(m.group(3)) if m.lastindex == 3 else lo
+    return {(m.group(1), r) for r in range(lo, hi + 1)}
+
+
+def _simulate_lds_waits(lines, in_flight):
+    """In-order LDS completion model: lgkmcnt(n) leaves at most the n most recent reads pending.
+    Fails if an MFMA or VALU instruction reads, or an LDS read overwrites, a register that a
+    pending LDS read still writes."""
+    pending = list(in_flight)  # register sets of reads not yet known complete, oldest first
+    for l in lines:
+        op = l.split()[0] if l.split() else ""
+        if op.startswith("ds_read"):
+            dst = _regset(l.split()[1].rstrip(","))
+            assert not any(dst & p for p in pending), f"LDS read overwrites a pending destination: {l}"
+            pending.append(dst)
+        elif op == "s_waitcnt" and "lgkmcnt(" in l:
+            n = int(l.split("lgkmcnt(")[1].rstrip(")"))
+            pending = pending[len(pending) - n:] if n < len(pending) else pending
+            if n == 0:
+                pending = []
+        elif op.startswith("v_"):
+            toks = [t.rstrip(",") for t in l.split()[1:]]
+            srcs = toks[1:] if op.startswith("v_mfma") else toks
+            for t in srcs:
+                if re.fullmatch(r"[va](\[\d+:\d+\]|\d+)", t):
+                    regs = _regset(t)
+                    assert not any(regs & p for p in pending), f"reads a register still being loaded: {l}"
+    return pending
+
+
+@pytest.mark.parametrize("gen", ["narrow", "wide"])
+def test_lds_waits_cover_every_fragment_use(gen):
+    mod = G if gen == "narrow" else GW
+    for has_next, masked in ((True, False), (True, True), (False, False)):
+        for parity in (0, 1):
+            A = mod.Asm()
+            if gen == "wide":
+                cur, nxt = (GW.V_SA, GW.V_SB) if parity == 0 else (GW.V_SB, GW.V_SA)
+                GW.block(A, cur, nxt, has_next, masked)
+                # entry state: K fragments 0..2 of the next tile in flight (issued before the barrier)
+                entry = [_regset(f"v[{GW.V_KF + 4 * i}:{GW.V_KF + 4 * i + 3}]") for i in range(3)] if has_next else []
+            else:
+                cur, nxt = (G.SA_BASE, G.SB_BASE) if parity == 0 else (G.SB_BASE, G.SA_BASE)
+                G.block(A, cur, nxt, 1 - parity, parity, has_next, masked)
+                entry = []
+            left = _simulate_lds_waits(A.lines, entry)
+            assert not left or gen == "wide", "narrow blocks leave no LDS read pending"
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="hipcc not available")
+def test_wide_operand_registers_do_not_overlap_loop_writes(tmp_path):
+    asm = tmp_path / "wide.s"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "--cuda-device-only", "-S",
+           "-o", str(asm), os.path.join(CSRC, "attn_bf16_d128_wide.hip")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    names = GW.check_operand_allocation(asm.read_text())
+    expected = {"ka%d" % i for i in range(8)} | {"va%d" % i for i in range(4)} | \
+               {"koff%d" % i for i in range(4)} | {"voff%d" % i for i in range(4)} | \
+               {"mrun0", "mrun1", "lrun0", "lrun1", "nmc0", "nmc1", "base2_0", "base2_1", "c", "thr", "nkt",
+                "tmask", "kvlim", "rowb", "kp_lo", "kp_hi", "vp_lo", "vp_hi", "tstride_lo", "tstride_hi",
+                "kdst0", "vdst0"}
     assert expected <= set(names), expected - set(names)

@@ -13,7 +13,7 @@ import torch
 import oracle
 import tensor_head_attention_amd as T
 import tha_workloads as W
-from parity import DEV, check_lse, check_out, say, to_dev
+from parity import DEV, check_lse, check_out, d128_kernel, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -57,20 +57,50 @@ def _id(c):
            f"{'_causal' if causal else ''}_qp{qp}_kp{kp}{'_pad' if lens else ''}"
 
 
-@pytest.mark.parametrize("case", CASES, ids=_id)
+# every case on the automatic choice; the bf16 head-size-128 cases also on each kernel forced
+KCASES = [(c, None) for c in CASES] + [(c, kn) for c in CASES if c[4] == 128 and c[5] == torch.bfloat16
+                                       for kn in ("narrow", "wide")]
+
+
+@pytest.mark.parametrize("case,kernel", KCASES, ids=lambda x: _id(x) if isinstance(x, tuple) else str(x))
 @pytest.mark.parametrize("out_f32", [False, True])
-def test_attn_matches_oracle(case, out_f32):
+def test_attn_matches_oracle(case, kernel, out_f32):
     B, Sq, Sk, H, D, dt, causal, qp, kp, lens = case
-    say(f"attn case {_id(case)} out_f32={out_f32}")
+    say(f"attn case {_id(case)} kernel={kernel} out_f32={out_f32}")
     q, k, v, kv = _inputs(B, Sq, Sk, H, D, dt, seed=Sq * 7 + Sk + D)
     ref, ref_lse = oracle.attention(q, k, v, causal=causal, q_pos0=qp, k_pos0=kp, kv_len=kv)
     qd, kd, vd = to_dev(q, k, v)
     kvd = kv.to(DEV) if kv is not None else None
-    out, lse = T.attn_fwd(qd, kd, vd, causal=causal, q_pos0=qp, k_pos0=kp, kv_len=kvd,
-                          out_dtype=torch.float32 if out_f32 else dt)
-    torch.cuda.synchronize()
+    with d128_kernel(kernel):
+        out, lse = T.attn_fwd(qd, kd, vd, causal=causal, q_pos0=qp, k_pos0=kp, kv_len=kvd,
+                              out_dtype=torch.float32 if out_f32 else dt)
+        torch.cuda.synchronize()
     check_out(out, ref, dt)
     check_lse(lse, ref_lse, dt)
+
+
+@pytest.mark.parametrize("shape", [(1, 600, 600, 3, True, 0, 0, None), (2, 513, 700, 2, False, 0, 0, [700, 333]),
+                                   (1, 300, 900, 2, True, 600, 0, None), (1, 1024, 1024, 8, True, 0, 0, None)])
+def test_attn_d128_kernels_bitwise_equal(shape):
+    """The narrow and wide head-size-128 kernels take the same arithmetic steps per row (same key
+    tile order, product order, softmax and row-sum order, rescale decisions), so their results
+    agree bit for bit; both also match the oracle."""
+    B, Sq, Sk, H, causal, qp, kp, lens = shape
+    say(f"narrow vs wide {shape}")
+    q, k, v, kv = _inputs(B, Sq, Sk, H, 128, torch.bfloat16, seed=Sq + 3 * Sk + H)
+    qd, kd, vd = to_dev(q, k, v)
+    kvd = kv.to(DEV) if kv is not None else None
+    res = {}
+    for kn in ("narrow", "wide"):
+        with d128_kernel(kn):
+            res[kn] = T.attn_fwd(qd, kd, vd, causal=causal, q_pos0=qp, k_pos0=kp, kv_len=kvd,
+                                 out_dtype=torch.float32)
+            torch.cuda.synchronize()
+    assert torch.equal(res["narrow"][0], res["wide"][0])
+    assert torch.equal(res["narrow"][1], res["wide"][1])
+    ref, ref_lse = oracle.attention(q, k, v, causal=causal, q_pos0=qp, k_pos0=kp, kv_len=kv)
+    check_out(res["wide"][0], ref, torch.bfloat16)
+    check_lse(res["wide"][1], ref_lse, torch.bfloat16)
 
 
 def test_attn_custom_scale_and_no_lse():

@@ -10,7 +10,7 @@ import torch
 import oracle
 import tensor_head_attention_amd as T
 import tha_workloads as W
-from parity import DEV, check_lse, check_out, say, to_dev
+from parity import DEV, check_lse, check_out, d128_kernel, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -81,8 +81,13 @@ def test_workload3_ulysses_share():
     del g7, dev
     qd, kd, vd = (grouped[n][0] for n in ("q", "k", "v"))
     q, k, v = (grouped[n][1] for n in ("q", "k", "v"))
-    out, lse = T.attn_fwd(qd, kd, vd, causal=True)
+    out, lse = T.attn_fwd(qd, kd, vd, causal=True)  # the wide kernel, as timed
     torch.cuda.synchronize()
+    with d128_kernel("narrow"):  # the other head-size-128 kernel gives the same bits
+        out_n, lse_n = T.attn_fwd(qd, kd, vd, causal=True)
+        torch.cuda.synchronize()
+    assert torch.equal(out_n, out) and torch.equal(lse_n, lse)
+    del out_n, lse_n
     Hl = H // P
     rows = _sample_rows(1, S, [4095, 4096, 8191, 8192, 16383, 16384, 28672], seed=33)
     ref, ref_lse = oracle.attention(q, k, v, causal=True, rows=rows)
@@ -127,6 +132,11 @@ def test_workload5_padded_batch():
     qd, kd, vd, kvd = to_dev(q, k, v, kv)
     out, lse = T.attn_fwd(qd, kd, vd, kv_len=kvd)
     torch.cuda.synchronize()
+    with d128_kernel("narrow"):
+        out_n, lse_n = T.attn_fwd(qd, kd, vd, kv_len=kvd)
+        torch.cuda.synchronize()
+    assert torch.equal(out_n, out) and torch.equal(lse_n, lse)
+    del out_n, lse_n
     lens = kv.tolist()
     extra = []
     for L in lens:
