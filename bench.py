@@ -44,19 +44,31 @@ def causal_pairs(Sq: int, Sk: int, q_pos0: int, k_pos0: int) -> int:
     return tot
 
 
+# Sources of the kernel that runs the timed attention (bf16, head size 128, a grid of >= 2
+# workgroups per CU): the wide kernel and its generated main loop.
+ATTN_KERNEL_SOURCES = ("attn_bf16_d128_wide.hip", "attn_loop_d128_wide.inc")
+
+
+def attn_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for name in ATTN_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "tensor_head_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def attn_traffic():
     """HBM bytes per attn_fwd dispatch from the committed rocprofv3 FETCH/WRITE summary, or None
-    when the kernel source has changed since those counters were taken."""
-    import hashlib
+    when the kernel sources have changed since those counters were taken."""
     path = os.path.join(ROOT, "profiles", "attn_fwd_ulysses32k_hbm_traffic.txt")
-    src = os.path.join(ROOT, "tensor_head_attention_amd", "csrc", "attn_bf16.hip")
     try:
         txt = open(path).read()
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        sha = attn_source_sha()
     except OSError:
         return None
     fields = dict(l.split(": ", 1) for l in txt.splitlines() if ": " in l)
-    if fields.get("attn_bf16.hip sha256 prefix", "").strip() != sha:
+    if fields.get("attn kernel sources sha256 prefix", "").strip() != sha:
         return None
     return float(fields["attn_fwd traffic_bytes_per_dispatch"])
 
@@ -173,7 +185,7 @@ def main():
                    "batch": 1, "seq_len": S, "heads": Hl, "head_dim": D, "shards": P, "group": grp,
                    "parallelism": "one GPU's Ulysses share"},
         "frac_of_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
-        "roofline": {"bound": "mfma", "kernel": "attn_fwd (attn_bf16_kernel<128, bf16>)",
+        "roofline": {"bound": "mfma", "kernel": "attn_fwd (attn_wide_kernel<bf16>, 256 query rows per workgroup)",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": attn_traffic(),
                      "avg_kernel_ms": round(attn_ms, 4)},
