@@ -138,30 +138,46 @@ def main():
         step(r)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    perm_ms = sum(r[0].elapsed_time(r[1]) for r in recs) / args.steps / 3.0   # one permute call
-    attn_ms = sum(r[1].elapsed_time(r[2]) for r in recs) / args.steps
+    perm_each = sorted(r[0].elapsed_time(r[1]) / 3.0 for r in recs)   # one permute call
+    attn_each = sorted(r[1].elapsed_time(r[2]) for r in recs)
+    perm_ms = sum(perm_each) / args.steps
+    attn_ms = sum(attn_each) / args.steps
     step_ms = sum(r[0].elapsed_time(r[2]) for r in recs) / args.steps
     step_ms = max(step_ms, wall * 1e3 / args.steps)
     value = flops / (step_ms * 1e-3) / 1e12
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
 
     components = {
-        "shard_permute": {"us_per_call": perm_ms * 1e3, "bytes_per_call": permute_bytes,
+        "shard_permute": {"us_per_call": perm_ms * 1e3, "us_median": perm_each[len(perm_each) // 2] * 1e3,
+                          "us_min": perm_each[0] * 1e3, "bytes_per_call": permute_bytes,
                           "GB_per_s": permute_bytes / (perm_ms * 1e-3) / 1e9,
                           "frac_hbm_peak": permute_bytes / (perm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
-        "attn_fwd": {"ms_per_call": attn_ms, "flop_per_call": flops, "TFLOP_per_s": attn_tflops,
+        "attn_fwd": {"ms_per_call": attn_ms, "ms_median": attn_each[len(attn_each) // 2], "ms_min": attn_each[0],
+                     "flop_per_call": flops, "TFLOP_per_s": attn_tflops,
                      "frac_mfma_peak": attn_tflops / PEAK_BF16_TFLOPS},
     }
 
-    # plain copy of known size (for scaling HBM counters of a profiled run)
+    # plain device copy of 256 MiB: the attainable streaming rate on this machine, and the known size
+    # that scales the HBM counters of a profiled run (the first copy)
     cp_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
     cp_dst = torch.empty_like(cp_src)
     cp_dst.copy_(cp_src)
     torch.cuda.synchronize()
+    cps = [(ev(), ev()) for _ in range(10)]
+    for a, b in cps:
+        a.record()
+        cp_dst.copy_(cp_src)
+        b.record()
+    torch.cuda.synchronize()
+    cp_ms = sorted(a.elapsed_time(b) for a, b in cps)[len(cps) // 2]
+    components["device_copy_256MiB"] = {"us_median": cp_ms * 1e3, "bytes": 2 * (256 << 20),
+                                        "GB_per_s": 2 * (256 << 20) / (cp_ms * 1e-3) / 1e9,
+                                        "frac_hbm_peak": 2 * (256 << 20) / (cp_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
     del cp_src, cp_dst
 
     if not args.no_side:
         components.update(ring_side(T, W, torch, dev, args.seed))
+        components.update(merge_rotating(T, torch, dev))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -241,6 +257,44 @@ def ring_side(T, W, torch, dev, seed):
     }
 
 
+def merge_rotating(T, torch, dev, n=8, S=4096, H=8, D=128, sets=3):
+    """8-way attn_merge_lse at the Ring share's shape, cycling over 3 independent sets of fp32
+    partials (3 x 128 MiB > the 256 MB MALL), so every call reads its partials from HBM."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    parts = [([torch.randn((1, S, H, D), generator=g, device=dev) for _ in range(n)],
+              [torch.randn((1, H, S), generator=g, device=dev) for _ in range(n)]) for _ in range(sets)]
+    out = torch.empty((1, S, H, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((1, H, S), dtype=torch.float32, device=dev)
+    for i in range(3):
+        T.attn_merge_lse(parts[i % sets][0], parts[i % sets][1], out=out, lse_out=lse)
+    reps = 30
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        T.attn_merge_lse(parts[i % sets][0], parts[i % sets][1], out=out, lse_out=lse)
+        b.record()
+    torch.cuda.synchronize()
+    each = sorted(a.elapsed_time(b) for a, b in evs)
+    ms = sum(each) / reps
+    nbytes = n * (S * H * D * 4 + H * S * 4) + S * H * D * 2 + H * S * 4
+    return {"attn_merge_lse_8way_hbm": {"us": ms * 1e3, "us_median": each[reps // 2] * 1e3, "us_min": each[0] * 1e3,
+                                        "bytes": nbytes, "GB_per_s": nbytes / (ms * 1e-3) / 1e9,
+                                        "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                        "inputs": f"{sets} rotating sets of {n} fp32 partials [1,{S},{H},{D}]"}}
+
+
+def cpu_model():
+    try:
+        for l in open("/proc/cpuinfo"):
+            if l.startswith("model name"):
+                return l.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def cpu_baseline(grouped, S, H, D, n_rows):
     """fp64 oracle on a sample of query rows of the same causal attention (all heads)."""
     import torch
@@ -257,7 +311,7 @@ def cpu_baseline(grouped, S, H, D, n_rows):
     return {"value": 4.0 * D * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": min(cores, n_rows), "kind": "oracle",
             "seconds": round(dt, 3),
             "sample": f"{n_rows} query rows evenly spaced over S={S} (all {H} heads, causal prefixes), "
-                      f"{pairs} visible pairs; fp64 two-pass oracle on {cores} host threads"}
+                      f"{pairs} visible pairs; fp64 two-pass oracle on {cores} host threads ({cpu_model()})"}
 
 
 if __name__ == "__main__":
