@@ -157,19 +157,23 @@ def main():
                      "frac_mfma_peak": attn_tflops / PEAK_BF16_TFLOPS},
     }
 
+    # shard_permute alone, timed in batches of back-to-back calls (Q, K, V shards in turn, as in
+    # the step; 3 x 64 MiB of distinct reads per round, so the reads come from HBM)
+    names = ("q", "k", "v")
+    pb = batch_times(torch, lambda i: T.shard_permute(shards[names[i % 3]], grp, out=grouped[names[i % 3]]))
+    components["shard_permute_batched"] = {"us_per_call": pb[len(pb) // 2] * 1e3, "us_min": pb[0] * 1e3,
+                                           "timing": BATCH_NOTE,
+                                           "GB_per_s": permute_bytes / (pb[len(pb) // 2] * 1e-3) / 1e9,
+                                           "frac_hbm_peak": permute_bytes / (pb[len(pb) // 2] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
     # plain device copy of 256 MiB: the attainable streaming rate on this machine, and the known size
     # that scales the HBM counters of a profiled run (the first copy)
     cp_src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
     cp_dst = torch.empty_like(cp_src)
     cp_dst.copy_(cp_src)
     torch.cuda.synchronize()
-    cps = [(ev(), ev()) for _ in range(10)]
-    for a, b in cps:
-        a.record()
-        cp_dst.copy_(cp_src)
-        b.record()
-    torch.cuda.synchronize()
-    cp_ms = sorted(a.elapsed_time(b) for a, b in cps)[len(cps) // 2]
+    cpt = batch_times(torch, lambda i: cp_dst.copy_(cp_src), batches=3, n=10)
+    cp_ms = cpt[len(cpt) // 2]
     components["device_copy_256MiB"] = {"us_median": cp_ms * 1e3, "bytes": 2 * (256 << 20),
                                         "GB_per_s": 2 * (256 << 20) / (cp_ms * 1e-3) / 1e9,
                                         "frac_hbm_peak": 2 * (256 << 20) / (cp_ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
@@ -211,6 +215,35 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+BATCH_NOTE = "median over 5 batches of 30 back-to-back calls, one event pair per batch"
+
+
+def batch_times(torch, call, batches=5, n=30):
+    """Per-call GPU time (ms) of a short kernel: `batches` batches of `n` back-to-back calls, each
+    batch between one pair of events, all queued behind a spin kernel.  Sorted ascending."""
+    for i in range(3):
+        call(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(batches)]
+    gpu_busy(torch)
+    i = 0
+    for a, b in evs:
+        a.record()
+        for _ in range(n):
+            call(i)
+            i += 1
+        b.record()
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) / n for a, b in evs)
+
+
+def gpu_busy(torch, ms=30.0):
+    """Queue a spin kernel of about `ms` on the current stream, so the short kernels timed after it
+    are all enqueued before the GPU reaches them: their event intervals then hold GPU time only,
+    not the host's per-call launch overhead."""
+    torch.cuda._sleep(int(ms * 1e-3 * 2.0e9))
+
+
 def ring_side(T, W, torch, dev, seed):
     """Ring share at the pages' shape: 8 chunk calls with fp32 partials + one 8-way merge."""
     inp, p = W.workload_inputs(4, seed=seed + 1)
@@ -241,6 +274,7 @@ def ring_side(T, W, torch, dev, seed):
     reps = 20
     recs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(reps)]
     torch.cuda.synchronize()
+    gpu_busy(torch)
     for r in recs:
         run(r)
     torch.cuda.synchronize()
@@ -268,18 +302,10 @@ def merge_rotating(T, torch, dev, n=8, S=4096, H=8, D=128, sets=3):
     lse = torch.empty((1, H, S), dtype=torch.float32, device=dev)
     for i in range(3):
         T.attn_merge_lse(parts[i % sets][0], parts[i % sets][1], out=out, lse_out=lse)
-    reps = 30
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    torch.cuda.synchronize()
-    for i, (a, b) in enumerate(evs):
-        a.record()
-        T.attn_merge_lse(parts[i % sets][0], parts[i % sets][1], out=out, lse_out=lse)
-        b.record()
-    torch.cuda.synchronize()
-    each = sorted(a.elapsed_time(b) for a, b in evs)
-    ms = sum(each) / reps
+    per = batch_times(torch, lambda i: T.attn_merge_lse(parts[i % sets][0], parts[i % sets][1], out=out, lse_out=lse))
+    ms = per[len(per) // 2]
     nbytes = n * (S * H * D * 4 + H * S * 4) + S * H * D * 2 + H * S * 4
-    return {"attn_merge_lse_8way_hbm": {"us": ms * 1e3, "us_median": each[reps // 2] * 1e3, "us_min": each[0] * 1e3,
+    return {"attn_merge_lse_8way_hbm": {"us": ms * 1e3, "us_min": per[0] * 1e3, "timing": BATCH_NOTE,
                                         "bytes": nbytes, "GB_per_s": nbytes / (ms * 1e-3) / 1e9,
                                         "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                                         "inputs": f"{sets} rotating sets of {n} fp32 partials [1,{S},{H},{D}]"}}

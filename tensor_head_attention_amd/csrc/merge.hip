@@ -55,18 +55,29 @@ __device__ __forceinline__ void store1(void* p, int64_t i, float v) {
 
 // Vector path (D % 4 == 0, D <= 1024, 8/16-byte aligned rows): each thread owns one chunk of 4
 // consecutive elements of one row; a row is `lanes` consecutive threads of the block (lanes a power
-// of two, <= 256).  Every thread reads the row's lse values before the block barrier and the row's
-// single lse store comes after it, so lse_out may alias lse_parts[0]; each output element is
-// written by the thread that read it, so o_out may alias o_parts[0].
+// of two, <= 256).  The data loads of the first 8 parts are issued before the lse reads, so a
+// workgroup waits for memory once rather than twice (lse, then data).  Every thread reads the row's
+// lse values before the block barrier and the row's single lse store comes after it, so lse_out may
+// alias lse_parts[0]; each output element is written by the thread that read it, so o_out may alias
+// o_parts[0].
 template <typename PartT, typename OutT>
 __global__ void __launch_bounds__(kThreads) merge_vec_kernel(PartPtrs parts, int n, void* o_out, float* lse_out,
                                                             int64_t rows, int S, int H, int D, int lanes_log2) {
+  constexpr int kChunk = 8;  // parts whose loads are in flight together
   const int lanes = 1 << lanes_log2;
   const int lane_in_row = threadIdx.x & (lanes - 1);
   const int64_t row = (int64_t)blockIdx.x * (kThreads >> lanes_log2) + (threadIdx.x >> lanes_log2);
   const bool live = row < rows;
+  const int c = lane_in_row * 4;
+  const int64_t off = row * D + c;
+  const bool act = live && c < D;
+  const int n0 = min(kChunk, n);
+  f32x4 x[kChunk];
+#pragma unroll
+  for (int u = 0; u < kChunk; ++u)
+    if (u < n0 && act) x[u] = Vec4<PartT>::load_nt(parts.o[u], off);
   int64_t li = 0;
-  float M = -INFINITY;
+  float M = -INFINITY, l0[kChunk];
   if (live) {
     // row = (b*S + s)*H + h  ->  lse index (b*H + h)*S + s
     const int64_t bs = row / H;
@@ -74,24 +85,32 @@ __global__ void __launch_bounds__(kThreads) merge_vec_kernel(PartPtrs parts, int
     const int64_t b = bs / S;
     const int s = (int)(bs - b * S);
     li = (b * H + h) * S + s;
-    for (int k = 0; k < n; ++k) M = fmaxf(M, parts.lse[k][li]);
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      l0[u] = u < n0 ? parts.lse[u][li] : -INFINITY;
+      M = fmaxf(M, l0[u]);
+    }
+    for (int k = kChunk; k < n; ++k) M = fmaxf(M, parts.lse[k][li]);
   }
   __syncthreads();  // all lse reads of the block precede its lse writes (in-place safety)
   if (!live) return;
-  const int c = lane_in_row * 4;
-  const int64_t off = row * D + c;
   if (M == -INFINITY) {
     if (c < D) Vec4<OutT>::store(o_out, off, f32x4{0.f, 0.f, 0.f, 0.f});
     if (lse_out && lane_in_row == 0) lse_out[li] = -INFINITY;
     return;
   }
-  // Parts in chunks of 8: all loads of a chunk in flight before its weights are applied.
-  constexpr int kChunk = 8;
   float W = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < n; k0 += kChunk) {
+#pragma unroll
+  for (int u = 0; u < kChunk; ++u)
+    if (u < n0) {
+      const float w = expf(l0[u] - M);
+      W += w;
+      if (c < D) acc += x[u] * w;
+    }
+  // further parts in chunks of 8: all loads of a chunk in flight before its weights are applied
+  for (int k0 = kChunk; k0 < n; k0 += kChunk) {
     const int kn = min(kChunk, n - k0);
-    f32x4 x[kChunk];
     float w[kChunk];
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
