@@ -52,8 +52,11 @@ def _load():
         lib.oracle_merge_lse.argtypes = [ctypes.c_int, vp, vp, i64, i64, i64, i64, dp, dp]
         lib.oracle_shard_permute.argtypes = [vp, ctypes.c_int, ctypes.c_int, i64, i64, i64, i64, ctypes.c_int, vp]
         lib.oracle_shard_unpermute.argtypes = [vp, ctypes.c_int, i64, i64, i64, i64, ctypes.c_int, vp]
+        lib.oracle_attention_backward.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64,
+                                                  ctypes.c_int, i64, i64, vp, ctypes.c_double, dp, dp, dp,
+                                                  ctypes.c_int]
         for f in (lib.oracle_attention, lib.oracle_attention_bruteforce, lib.oracle_merge_lse,
-                  lib.oracle_shard_permute, lib.oracle_shard_unpermute):
+                  lib.oracle_shard_permute, lib.oracle_shard_unpermute, lib.oracle_attention_backward):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -123,6 +126,34 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool
     if rows is None:
         return out.view(B, Sq, H, D), lse.view(B, Sq, H).permute(0, 2, 1).contiguous()
     return out, lse
+
+
+def attention_backward(q, k, v, dout, *, causal: bool = False, q_pos0: int = 0, k_pos0: int = 0,
+                       kv_len: Optional[torch.Tensor] = None, scale: Optional[float] = None, nthreads: int = 0):
+    """fp64 gradients (dq, dk, dv) of attention for the cotangent dout (same masks and positions
+    as attention()).  q, dout: [B, Sq, H, D]; k, v: [B, Sk, H, D]; float32 or bfloat16, one dtype.
+    Returns float64 tensors dq [B, Sq, H, D], dk [B, Sk, H, D], dv [B, Sk, H, D]."""
+    q, k, v, dout = _host(q), _host(k), _host(v), _host(dout)
+    dt = _dtype_code(q)
+    if any(_dtype_code(t) != dt for t in (k, v, dout)):
+        raise TypeError("q, k, v, dout must share one dtype")
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    if tuple(k.shape) != (B, Sk, H, D) or tuple(v.shape) != tuple(k.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("shape mismatch")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    kl = _host(kv_len.to(torch.int32)) if kv_len is not None else None
+    dq = torch.empty((B, Sq, H, D), dtype=torch.float64)
+    dk = torch.empty((B, Sk, H, D), dtype=torch.float64)
+    dv = torch.empty((B, Sk, H, D), dtype=torch.float64)
+    rc = _load().oracle_attention_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), dt,
+                                           B, Sq, Sk, H, D, int(bool(causal)), int(q_pos0), int(k_pos0),
+                                           kl.data_ptr() if kl is not None else None, float(scale),
+                                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle_attention_backward rejected its arguments")
+    return dq, dk, dv
 
 
 def attention_bruteforce(q, k, v, *, causal=False, q_pos0=0, k_pos0=0, kv_len=None, scale=None):

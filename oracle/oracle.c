@@ -338,3 +338,131 @@ int oracle_shard_unpermute(const void* const* groups, int P, int64_t B, int64_t 
             }
   return 0;
 }
+
+/* ---- attention backward (the vector-Jacobian product of attention) ------ */
+
+/*
+ * The gradients of a scalar loss L through attention, given dout = dL/dout.
+ * Nothing on the pages writes these out; they are the derivative of the forward
+ * definition above (reading: the chain rule through softmax), which is what the
+ * pages' training workloads ("Support deepspeed sequence parallel", a training
+ * script; "关于数据分割和合并", the gradient of the attention output) need.
+ * Per (b, h), over visible pairs (i, j) only:
+ *   P_ij  = softmax_j(s_i),  s_ij = scale * q_i . k_j
+ *   dV_j  = sum_i P_ij dout_i
+ *   dP_ij = dout_i . v_j
+ *   dS_ij = P_ij * (dP_ij - sum_l P_il dP_il)       (Jacobian of softmax)
+ *   dQ_i  = scale * sum_j dS_ij k_j
+ *   dK_j  = scale * sum_i dS_ij q_i
+ * A query row with no visible key contributes nothing (its output is the
+ * constant 0).
+ */
+typedef struct {
+  const void *q, *k, *v, *dout;
+  int dtype;
+  int64_t B, Sq, Sk, H, D;
+  int causal;
+  int64_t q_pos0, k_pos0;
+  const int32_t* kv_len;
+  double scale;
+  double *dq, *dk, *dv; /* [B,Sq,H,D], [B,Sk,H,D], [B,Sk,H,D] */
+  int64_t next;         /* work counter over (b, h), guarded by mu */
+  pthread_mutex_t mu;
+} bwd_job;
+
+static double qkv(const bwd_job* J, const void* t, int64_t b, int64_t s, int64_t S, int64_t h, int64_t d) {
+  return elem_to_double(t, J->dtype, bshd(b, s, h, d, S, J->H, J->D));
+}
+
+/* All query rows of one (b, h); dk / dv of this (b, h) are owned by the caller's thread. */
+static void bwd_head(bwd_job* J, int64_t b, int64_t h, double* P, double* dP) {
+  const int64_t Sq = J->Sq, Sk = J->Sk, D = J->D;
+  const int64_t len_b = clamp_len(J->kv_len, b, Sk);
+  for (int64_t i = 0; i < Sq; ++i) {
+    /* the softmax row P_i (two passes: max, then normalised exponentials) */
+    double m = -INFINITY;
+    for (int64_t j = 0; j < Sk; ++j) {
+      if (!visible(J->causal, J->q_pos0, J->k_pos0, i, j, len_b)) {
+        P[j] = -INFINITY;
+        continue;
+      }
+      double dot = 0.0;
+      for (int64_t d = 0; d < D; ++d) dot += qkv(J, J->q, b, i, Sq, h, d) * qkv(J, J->k, b, j, Sk, h, d);
+      P[j] = dot * J->scale;
+      if (P[j] > m) m = P[j];
+    }
+    for (int64_t d = 0; d < D; ++d) J->dq[bshd(b, i, h, d, Sq, J->H, D)] = 0.0;
+    if (m == -INFINITY) continue; /* no visible key */
+    double z = 0.0;
+    for (int64_t j = 0; j < Sk; ++j) z += P[j] == -INFINITY ? 0.0 : exp(P[j] - m);
+    for (int64_t j = 0; j < Sk; ++j) P[j] = P[j] == -INFINITY ? 0.0 : exp(P[j] - m) / z;
+    /* dP_ij = dout_i . v_j and the row's sum_l P_il dP_il */
+    double delta = 0.0;
+    for (int64_t j = 0; j < Sk; ++j) {
+      if (P[j] == 0.0) {
+        dP[j] = 0.0;
+        continue;
+      }
+      double dot = 0.0;
+      for (int64_t d = 0; d < D; ++d) dot += qkv(J, J->dout, b, i, Sq, h, d) * qkv(J, J->v, b, j, Sk, h, d);
+      dP[j] = dot;
+      delta += P[j] * dot;
+    }
+    for (int64_t j = 0; j < Sk; ++j) {
+      if (P[j] == 0.0) continue;
+      const double ds = P[j] * (dP[j] - delta);
+      for (int64_t d = 0; d < D; ++d) {
+        J->dq[bshd(b, i, h, d, Sq, J->H, D)] += J->scale * ds * qkv(J, J->k, b, j, Sk, h, d);
+        J->dk[bshd(b, j, h, d, Sk, J->H, D)] += J->scale * ds * qkv(J, J->q, b, i, Sq, h, d);
+        J->dv[bshd(b, j, h, d, Sk, J->H, D)] += P[j] * qkv(J, J->dout, b, i, Sq, h, d);
+      }
+    }
+  }
+}
+
+static void* bwd_worker(void* arg) {
+  bwd_job* J = (bwd_job*)arg;
+  double* P = (double*)malloc(sizeof(double) * (size_t)J->Sk);
+  double* dP = (double*)malloc(sizeof(double) * (size_t)J->Sk);
+  for (;;) {
+    pthread_mutex_lock(&J->mu);
+    int64_t w = J->next++;
+    pthread_mutex_unlock(&J->mu);
+    if (w >= J->B * J->H) break;
+    bwd_head(J, w / J->H, w % J->H, P, dP);
+  }
+  free(P);
+  free(dP);
+  return NULL;
+}
+
+/*
+ * oracle_attention_backward: dq [B,Sq,H,D], dk and dv [B,Sk,H,D] (double, overwritten) for
+ * inputs q [B,Sq,H,D], k, v [B,Sk,H,D] and dout [B,Sq,H,D] of element type dtype, with the
+ * same masks, positions and scale as oracle_attention.  Returns 0, or -1 on a bad argument.
+ */
+int oracle_attention_backward(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                              int64_t B, int64_t Sq, int64_t Sk, int64_t H, int64_t D, int causal,
+                              int64_t q_pos0, int64_t k_pos0, const int32_t* kv_len, double scale,
+                              double* dq, double* dk, double* dv, int nthreads) {
+  if (!q || !k || !v || !dout || !dq || !dk || !dv || B <= 0 || Sq <= 0 || Sk <= 0 || H <= 0 || D <= 0)
+    return -1;
+  if (dtype != ORACLE_F32 && dtype != ORACLE_BF16) return -1;
+  for (size_t i = 0; i < (size_t)(B * Sk * H * D); ++i) dk[i] = dv[i] = 0.0;
+  bwd_job J;
+  memset(&J, 0, sizeof J);
+  J.q = q, J.k = k, J.v = v, J.dout = dout, J.dtype = dtype;
+  J.B = B, J.Sq = Sq, J.Sk = Sk, J.H = H, J.D = D;
+  J.causal = causal, J.q_pos0 = q_pos0, J.k_pos0 = k_pos0, J.kv_len = kv_len, J.scale = scale;
+  J.dq = dq, J.dk = dk, J.dv = dv, J.next = 0;
+  pthread_mutex_init(&J.mu, NULL);
+  int nt = pick_threads(nthreads);
+  if (nt > B * H) nt = (int)(B * H);
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nt);
+  for (int t = 1; t < nt; ++t) pthread_create(&th[t], NULL, bwd_worker, &J);
+  bwd_worker(&J);
+  for (int t = 1; t < nt; ++t) pthread_join(th[t], NULL);
+  free(th);
+  pthread_mutex_destroy(&J.mu);
+  return 0;
+}

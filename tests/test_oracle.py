@@ -351,3 +351,91 @@ def test_oracle_rejects_bad_arguments():
         oracle.shard_permute([torch.zeros(1, 2, 3, 4)] * 2, 0)  # H=3 not divisible by P=2
     with pytest.raises(ValueError):
         oracle.shard_permute([torch.zeros(1, 2, 4, 4)] * 2, 2)  # group out of range
+
+
+# ---- attention backward ----------------------------------------------------------------------
+
+def _dyadic(shape, g, lo=-24, hi=24):
+    """fp32 values that are multiples of 2^-8 (so +-2^-10 perturbations are exact in fp32)."""
+    return torch.randint(lo, hi + 1, shape, generator=g).to(torch.float32) / 256.0
+
+
+def _loss(q, k, v, dout, **kw):
+    out, _ = oracle.attention(q, k, v, **kw)
+    return float((out * dout.double()).sum())
+
+
+@pytest.mark.parametrize("kw", [dict(causal=True, q_pos0=1, k_pos0=0),
+                                dict(causal=False, kv_len=torch.tensor([3, 5], dtype=torch.int32)),
+                                dict(causal=True, q_pos0=0, k_pos0=2)])  # first rows see no key
+def test_backward_matches_finite_differences(kw):
+    """Central differences of the forward oracle's L = sum(dout * out) against every element of
+    the analytic dq, dk, dv (the chain rule through softmax)."""
+    g = torch.Generator().manual_seed(71)
+    B = 2 if "kv_len" in kw else 1
+    q, k, v = _dyadic((B, 4, 2, 3), g), _dyadic((B, 5, 2, 3), g), _dyadic((B, 5, 2, 3), g)
+    dout = _dyadic((B, 4, 2, 3), g)
+    dq, dk, dv = oracle.attention_backward(q, k, v, dout, **kw)
+    h = 2.0 ** -10
+    for name, t, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        flat = t.view(-1)
+        num = torch.empty(flat.numel(), dtype=torch.float64)
+        for e in range(flat.numel()):
+            x0 = float(flat[e])
+            flat[e] = x0 + h
+            lp = _loss(q, k, v, dout, **kw)
+            flat[e] = x0 - h
+            lm = _loss(q, k, v, dout, **kw)
+            flat[e] = x0
+            num[e] = (lp - lm) / (2 * h)
+        assert torch.allclose(grad.reshape(-1), num, rtol=1e-5, atol=1e-6), (name, (grad.reshape(-1) - num).abs().max())
+
+
+def _torch_attention_grads(q, k, v, dout, causal, q_pos0, k_pos0, kv_len, scale):
+    """fp64 autograd of attention written with plain torch ops (every row must see a key)."""
+    q, k, v = (t.double().requires_grad_(True) for t in (q, k, v))
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    s = torch.einsum("bihd,bjhd->bhij", q, k) * scale
+    i = torch.arange(Sq).view(Sq, 1)
+    j = torch.arange(Sk).view(1, Sk)
+    vis = torch.ones(B, 1, Sq, Sk, dtype=torch.bool)
+    if causal:
+        vis = vis & (k_pos0 + j <= q_pos0 + i)
+    if kv_len is not None:
+        vis = vis & (j < kv_len.view(B, 1, 1, 1).long())
+    s = s.masked_fill(~vis, float("-inf"))
+    out = torch.einsum("bhij,bjhd->bihd", torch.softmax(s, dim=-1), v)
+    (out * dout.double()).sum().backward()
+    return q.grad, k.grad, v.grad
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_backward_matches_fp64_autograd(dtype):
+    """The oracle's gradients equal fp64 torch autograd through a plain attention (a library
+    routine on the same fp64 values)."""
+    g = W.generator(72)
+    B, Sq, Sk, H, D = 2, 33, 40, 3, 16
+    q, k, v, dout = (W.randn(s, g, dtype) for s in ((B, Sq, H, D), (B, Sk, H, D), (B, Sk, H, D), (B, Sq, H, D)))
+    kv = torch.tensor([40, 29], dtype=torch.int32)
+    for causal, qp, kp, kl in ((True, 7, 0, None), (False, 0, 0, kv), (True, 10, 3, kv)):
+        dq, dk, dv = oracle.attention_backward(q, k, v, dout, causal=causal, q_pos0=qp, k_pos0=kp, kv_len=kl)
+        tq, tk, tv = _torch_attention_grads(q, k, v, dout, causal, qp, kp, kl, 1.0 / math.sqrt(D))
+        for a, b in ((dq, tq), (dk, tk), (dv, tv)):
+            assert torch.allclose(a, b, rtol=1e-10, atol=1e-12)
+
+
+def test_backward_invariants():
+    """Closed forms: sum over keys of dK is 0 (each softmax row's dS sums to 0); sum over keys of
+    dV equals the sum of dout over rows that see a key; V = 0 gives dQ = dK = 0; a row with no
+    visible key gets dQ = 0."""
+    g = W.generator(73)
+    B, Sq, Sk, H, D = 1, 20, 24, 2, 8
+    q, k, v, dout = (W.randn(s, g, torch.float32) for s in ((B, Sq, H, D), (B, Sk, H, D), (B, Sk, H, D), (B, Sq, H, D)))
+    dq, dk, dv = oracle.attention_backward(q, k, v, dout, causal=True, q_pos0=0, k_pos0=5)
+    # rows i < 5 see no key (k_pos0 + j <= i needs i >= 5)
+    assert torch.all(dq[:, :5] == 0)
+    assert dk.sum(dim=1).abs().max() < 1e-12
+    assert torch.allclose(dv.sum(dim=1), dout[:, 5:].double().sum(dim=1), atol=1e-12)
+    dq0, dk0, _ = oracle.attention_backward(q, k, torch.zeros_like(v), dout, causal=True)
+    assert torch.all(dq0 == 0) and torch.all(dk0 == 0)
