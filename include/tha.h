@@ -105,6 +105,37 @@ THA_API int attn_fwd(const void* q, const void* k, const void* v, void* o, int o
              const int* kv_len, float scale, void* stream);
 
 /*
+ * attn_bwd -- gradients of attn_fwd with respect to q, k and v for the cotangent
+ * dout = dL/do.  The pages' workloads are training ("Support deepspeed sequence
+ * parallel", a training script; "关于数据分割和合并", the gradient of the attention
+ * output); the formulas are the chain rule through attn_fwd's softmax (a reading:
+ * the pages do not write them out).  With P the softmax of attn_fwd (same masks,
+ * positions and scale), dP_ij = dout_i . v_j and Delta_i = dout_i . o_i:
+ *   dv_j += sum_i P_ij dout_i
+ *   dq_i += scale * sum_j P_ij (dP_ij - Delta_i) k_j
+ *   dk_j += scale * sum_i P_ij (dP_ij - Delta_i) q_i
+ * o and lse must be attn_fwd's output and lse of the same query rows over their
+ * FULL key set (for a Ring share: the merged o and lse), so that P is recovered
+ * exactly as exp(scale q.k - lse) and Delta_i equals sum_j P_ij dP_ij.
+ *
+ * q, o, dout: [B,Sq,H,D]; k, v: [B,Sk,H,D], all of element type in_dt; lse
+ * [B,H,Sq] fp32.  dq [B,Sq,H,D], dk and dv [B,Sk,H,D] are fp32 and ACCUMULATED
+ * into: zero them for a plain backward; the steps of a Ring share add their
+ * partial gradients into the same buffers.  workspace: device fp32 array of at
+ * least B*H*Sq elements owned by the caller, overwritten (it holds Delta).
+ * Masks, positions, kv_len and scale as in attn_fwd.
+ * Supported: in_dt = THA_BF16 with D = 64 or 128 (matrix-core path: bf16
+ * products with fp32 accumulation, P and dS rounded to bf16 as operands of the
+ * products that consume them); in_dt = THA_F32 with 1 <= D <= 256 (fp32
+ * throughout).
+ * Errors: as attn_fwd, plus THA_ERR_INVALID for a null o, dout, lse, dq, dk, dv
+ * or workspace.
+ */
+THA_API int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+             float* dq, float* dk, float* dv, float* workspace, int B, int Sq, int Sk, int H, int D, int in_dt,
+             unsigned mask_flags, long long q_pos0, long long k_pos0, const int* kv_len, float scale, void* stream);
+
+/*
  * attn_merge_lse -- combine n partial attention results over disjoint key
  * sets into the result over their union (the Ring step "accumulate block
  * results into the full attention", "adv07: Sequence Parallel" Q5; the

@@ -42,10 +42,13 @@ def load_library(path: str = LIB_PATH):
     vp, ci, cll = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, ci, vp, ci, ci, ci, ci, ci, ci, ctypes.c_uint, cll, cll, vp,
                              ctypes.c_float, vp]
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_uint, cll, cll,
+                             vp, ctypes.c_float, vp]
     lib.attn_merge_lse.argtypes = [ci, vp, vp, ci, vp, ci, vp, ci, ci, ci, ci, vp]
     lib.shard_permute.argtypes = [vp, ci, ci, vp, ci, ci, ci, ci, ci, vp]
     lib.shard_unpermute.argtypes = [vp, ci, ci, vp, ci, ci, ci, ci, ci, vp]
-    for f in (lib.attn_fwd, lib.attn_merge_lse, lib.shard_permute, lib.shard_unpermute, lib.tha_version):
+    for f in (lib.attn_fwd, lib.attn_bwd, lib.attn_merge_lse, lib.shard_permute, lib.shard_unpermute,
+              lib.tha_version):
         f.restype = ci
     lib.tha_status_string.argtypes = [ci]
     lib.tha_status_string.restype = ctypes.c_char_p
@@ -125,6 +128,52 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool 
                        int(q_pos0), int(k_pos0), kvp, float(scale), _stream(q))
     _check(rc, "attn_fwd")
     return (out, lse) if return_lse else out
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,
+             lse: torch.Tensor, *, causal: bool = False, kv_len: Optional[torch.Tensor] = None, q_pos0: int = 0,
+             k_pos0: int = 0, scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
+             dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None):
+    """Gradients of attn_fwd (see tha.h attn_bwd): returns (dq, dk, dv), fp32.  Given dq / dk / dv
+    are accumulated into; missing ones start from zero.  workspace: fp32 of >= B*H*Sq elements."""
+    load_library()
+    q, k, v, o, dout, lse = (_dev(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"),
+                                                        (lse, "lse")))
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    if lse.dtype != torch.float32:
+        raise ValueError("lse must be float32")
+    if dq is None:
+        dq = torch.zeros((B, Sq, H, D), dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.zeros((B, Sk, H, D), dtype=torch.float32, device=q.device)
+    if dv is None:
+        dv = torch.zeros((B, Sk, H, D), dtype=torch.float32, device=q.device)
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _dev(t, n)
+        if t.dtype != torch.float32:
+            raise ValueError(f"{n} must be float32")
+    if workspace is None:
+        workspace = torch.empty((B * H * Sq,), dtype=torch.float32, device=q.device)
+    if workspace.dtype != torch.float32 or workspace.numel() < B * H * Sq:
+        raise ValueError("workspace must be float32 with at least B*H*Sq elements")
+    _dev(workspace, "workspace")
+    flags = THA_MASK_CAUSAL if causal else 0
+    kvp = None
+    if kv_len is not None:
+        kv_len = _dev(kv_len, "kv_len")
+        if kv_len.dtype != torch.int32:
+            raise ValueError("kv_len must be int32")
+        flags |= THA_MASK_KEY_PADDING
+        kvp = kv_len.data_ptr()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rc = _lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, Sq, Sk, H, D,
+                       _dt(q.dtype), flags, int(q_pos0), int(k_pos0), kvp, float(scale), _stream(q))
+    _check(rc, "attn_bwd")
+    return dq, dk, dv
 
 
 def attn_merge_lse(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Tensor], *,

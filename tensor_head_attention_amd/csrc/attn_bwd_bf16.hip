@@ -1,0 +1,453 @@
+// attn_bwd_bf16.hip -- attention backward on bf16 matrix cores (gfx950), head size 64 or 128.
+//
+// Gradients of the attention of attn_bf16*.hip for the cotangent dout (the chain rule through
+// the softmax; the pages' training workloads need them, "Support deepspeed sequence parallel" and
+// "关于数据分割和合并"; the formulas are a reading):
+//   P_ij = exp(scale q_i . k_j - lse_i),  dP_ij = dout_i . v_j,  dS_ij = P_ij (dP_ij - Delta_i)
+//   dv_j += sum_i P_ij dout_i,  dq_i += scale sum_j dS_ij k_j,  dk_j += scale sum_i dS_ij q_i
+// with lse from the forward pass and Delta_i = dout_i . o_i from the pre-pass (attn_bwd_f32.hip).
+// Products run on v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dS are rounded to bf16
+// as operands of the products that consume them (as the forward rounds P before P V).
+//
+// Two kernels, neither needs atomics, so results are deterministic:
+//  * dq: a workgroup owns 128 query rows (4 wavefronts x 32) of one (b, h) and streams 64-key
+//    tiles of K and V through LDS, as the forward kernels do.  Per tile a wavefront computes
+//    S^T = K Q^T and dP^T = V dO^T (Q^T and dO^T are register-resident B operands), P^T and dS^T
+//    in the accumulator layout (one query per lane, so lse and Delta are per-lane scalars), and
+//    dQ^T += K^T dS^T with K^T read from the row-major K tile by ds_read_b64_tr_b16.
+//  * dk/dv: a workgroup owns 128 keys (4 wavefronts x 32) and streams 64-query tiles of Q and
+//    dO.  Per tile: S = Q K^T and dP = dO V^T (K^T and V^T register-resident), P and dS in the
+//    accumulator layout (one key per lane; the 16 queries a lane holds read their lse and Delta
+//    from LDS as four 4-wide vectors), dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T read
+//    by ds_read_b64_tr_b16.
+// The accumulator layout puts the 16 rows of a 16-step in the order {0-3, 8-11} / {4-7, 12-15}
+// between the half-waves; the transposing reads address the matching rows, so packed P / dS
+// feed the next product directly (as in the forward kernels).
+// Tiles read both row-wise (ds_read_b128 of 32 rows x one 16-byte chunk) and transposed (4 rows
+// x 4 chunks per half-wave) use one XOR swizzle of the chunk index that is a bijection for both
+// patterns: D = 128: chunk ^ ((row & 3) << 2 | (row >> 2) & 3); D = 64 (two rows per bank line):
+// chunk ^ (((row >> 1) & 1) << 2 | (row >> 2) & 3).  Tiles are copied by buffer_load ... lds,
+// double buffered.  Both kernels launch heaviest causal blocks first.
+#include "device_common.h"
+#include "tha_kernels.h"
+
+namespace tha {
+
+namespace {
+
+constexpr int kWaves = 4, kThreads = kWaves * 64;
+constexpr int kRowsPerWave = 32;
+constexpr int kBlockRows = kWaves * kRowsPerWave;  // owned rows per workgroup
+constexpr int kTile = 64;                          // streamed rows per LDS tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (D == 128)
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  else
+    return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
+
+struct KArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* dout;
+  const float* lse;
+  const float* delta;
+  float* dq;
+  float* dk;
+  float* dv;
+  const int* kv_len;
+  int B, Sq, Sk, H;
+  int causal;
+  long long q_pos0, k_pos0;
+  float scale, scale_log2;
+};
+
+__device__ __forceinline__ int clamp_kv(const int* kv_len, int b, int Sk) {
+  if (!kv_len) return Sk;
+  const int L = kv_len[b];
+  return L < 0 ? 0 : (L > Sk ? Sk : L);
+}
+
+// Per-lane offsets for copying a 64-row tile (rows of row_bytes, D bf16) into LDS, swizzled on
+// the global side so the LDS side is written linearly: wave w issues D/32 copies of 512/D rows.
+template <int D>
+struct TileCopy {
+  static constexpr int kLoads = D / 32;       // per wave per tile
+  static constexpr int kRowsPerLoad = 512 / D;
+  static constexpr int kChunks = D / 8;
+  uint32_t off[kLoads];
+  __device__ void init(int wave, int lane, uint32_t row_bytes) {
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) {
+      const int r = (wave * kLoads + u) * kRowsPerLoad + lane / kChunks;
+      const int p = lane % kChunks;
+      off[u] = (uint32_t)r * row_bytes + (uint32_t)((p ^ swz<D>(r)) * 16);
+    }
+  }
+  // rows [row0, row0 + 64) of a tensor whose row 0 is at base; rows >= valid_end read 0
+  __device__ void copy(const __bf16* base, int64_t row_stride, int row0, int valid_end, char* dst, int wave) const {
+    const int rows_valid = min(kTile, valid_end - row0);
+    const i32x4 rs = make_rsrc_words(base + (int64_t)row0 * row_stride,
+                                     (uint32_t)max(rows_valid, 0) * (uint32_t)(row_stride * 2));
+    const uint32_t l = lds_addr(dst + wave * kLoads * 1024);
+#pragma unroll
+    for (int u = 0; u < kLoads; ++u) buffer_load_lds_16(rs, l + u * 1024, off[u]);
+  }
+};
+
+// Row-fragment read (A operand from rows): row rb*32 + lq, logical chunk 2t + hi.
+template <int D>
+__device__ __forceinline__ bf16x8 row_frag(const char* tile, int lq, int hi, int rb, int t) {
+  const int row = rb * 32 + lq;
+  return *(const bf16x8*)(tile + row * (D * 2) + (((2 * t + hi) ^ swz<D>(row)) * 16));
+}
+
+// Transposed fragment (A operand [dim][row]): 16-row step ks, 32-dim block db.  Lane (g, sl)
+// reads rows 16ks + 4hi + sl/4 and +8, dims 32db + 16(g&1) + 4(sl&3) .. +3.
+template <int D>
+__device__ __forceinline__ bf16x8 tr_frag(const char* tile, int lane, int ks, int db) {
+  const int g = lane >> 4, sl = lane & 15, hi = lane >> 5;
+  const int c = 4 * db + 2 * (g & 1) + ((sl & 3) >> 1);
+  const int r0 = 16 * ks + 4 * hi + (sl >> 2), r1 = r0 + 8;
+  const int byte_in = (sl & 1) * 8;
+  const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(tile + r0 * (D * 2) + ((c ^ swz<D>(r0)) * 16) + byte_in));
+  const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)(tile + r1 * (D * 2) + ((c ^ swz<D>(r1)) * 16) + byte_in));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// B-operand fragments of 32 register-resident rows (row r0 + lq): dims 16t + 8hi .. +7.
+template <int D>
+__device__ __forceinline__ void load_rows(bf16x8 (&f)[D / 16], const __bf16* base, int64_t row_stride, int r0,
+                                          int valid_end, int lq, int hi) {
+  const int rows_valid = max(0, min(kRowsPerWave, valid_end - r0));
+  const uint32_t row_bytes = (uint32_t)(row_stride * 2);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (int64_t)min(r0, max(valid_end - 1, 0)) * row_stride,
+                                              (uint32_t)rows_valid * row_bytes);
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t)
+    f[t] = __builtin_bit_cast(bf16x8, buffer_load_16(rs, (uint32_t)lq * row_bytes + (uint32_t)(16 * t + 8 * hi) * 2));
+}
+
+// Pack accumulator elements 8h..8h+7 of block kb into the B operand of a 16-row step.
+__device__ __forceinline__ bf16x8 pack8(const f32x16& x, int h) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[8 * h + e];
+  return r;
+}
+
+// ---------------------------------------------------------------------------------------------
+// dq: 128 query rows per workgroup, 64-key tiles.
+template <int D>
+__global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(KArgs a) {
+  constexpr int kDSteps = D / 16, kDBlocks = D / 32, kTileBytes = kTile * D * 2;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];  // K[0], K[1], V[0], V[1]
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lq = lane & 31, hi = lane >> 5;
+  const int BH = a.B * a.H;
+  const int n_qt = (a.Sq + kBlockRows - 1) / kBlockRows;
+  const int qt = n_qt - 1 - (int)(blockIdx.x / BH);
+  const int bh = (int)(blockIdx.x % BH);
+  const int b = bh / a.H, h = bh % a.H;
+  const int64_t rs = (int64_t)a.H * D;
+  const int kv_lim = clamp_kv(a.kv_len, b, a.Sk);
+  long long kv_end = kv_lim;
+  const int q_first = qt * kBlockRows;
+  if (a.causal) {
+    const int q_last = min(a.Sq, q_first + kBlockRows) - 1;
+    const long long last_vis = a.q_pos0 + q_last - a.k_pos0;
+    if (last_vis + 1 < kv_end) kv_end = last_vis + 1 < 0 ? 0 : last_vis + 1;
+  }
+  const int n_kt = (int)((kv_end + kTile - 1) / kTile);
+
+  const int q0 = q_first + wave * kRowsPerWave;
+  const __bf16* qbase = a.q + (int64_t)b * a.Sq * rs + (int64_t)h * D;
+  const __bf16* dbase = a.dout + (int64_t)b * a.Sq * rs + (int64_t)h * D;
+  bf16x8 qf[kDSteps], df[kDSteps];
+  load_rows<D>(qf, qbase, rs, q0, a.Sq, lq, hi);
+  load_rows<D>(df, dbase, rs, q0, a.Sq, lq, hi);
+  const int qrow = q0 + lq;
+  float Lc = INFINITY, Dl = 0.f;  // P = exp2(s*c - Lc); +inf gives 0 (no key, or a row past Sq)
+  if (qrow < a.Sq) {
+    const float L = a.lse[(int64_t)bh * a.Sq + qrow];
+    Lc = L == -INFINITY ? INFINITY : L * kLog2e;
+    Dl = a.delta[(int64_t)bh * a.Sq + qrow];
+  }
+  long long lim_abs = kv_lim;  // key index visible to this lane's query iff key < lim_abs
+  if (a.causal) {
+    const long long c = a.q_pos0 + qrow - a.k_pos0 + 1;
+    lim_abs = c < lim_abs ? c : lim_abs;
+  }
+
+  TileCopy<D> cp;
+  cp.init(wave, lane, (uint32_t)(rs * 2));
+  const __bf16* kbase = a.k + (int64_t)b * a.Sk * rs + (int64_t)h * D;
+  const __bf16* vbase = a.v + (int64_t)b * a.Sk * rs + (int64_t)h * D;
+  char* const kbuf = smem;
+  char* const vbuf = smem + 2 * kTileBytes;
+
+  f32x16 acc[kDBlocks];
+#pragma unroll
+  for (int i = 0; i < kDBlocks; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[i][j] = 0.f;
+
+  if (n_kt > 0) {
+    cp.copy(kbase, rs, 0, kv_lim, kbuf, wave);
+    cp.copy(vbase, rs, 0, kv_lim, vbuf, wave);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < n_kt) {
+      cp.copy(kbase, rs, (kt + 1) * kTile, kv_lim, kbuf + (buf ^ 1) * kTileBytes, wave);
+      cp.copy(vbase, rs, (kt + 1) * kTile, kv_lim, vbuf + (buf ^ 1) * kTileBytes, wave);
+    }
+    const int key0 = kt * kTile;
+    bool skip = q0 >= a.Sq;
+    bool need_mask = key0 + kTile > kv_lim;
+    if (a.causal) {
+      const long long first_kpos = a.k_pos0 + key0;
+      if (first_kpos > a.q_pos0 + q0 + kRowsPerWave - 1) skip = true;
+      if (first_kpos + kTile - 1 > a.q_pos0 + q0) need_mask = true;
+    }
+    if (!skip) {
+      const char* kt_ = kbuf + buf * kTileBytes;
+      const char* vt_ = vbuf + buf * kTileBytes;
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) s[kb][j] = dp[kb][j] = 0.f;
+#pragma unroll
+        for (int t = 0; t < kDSteps; ++t) {
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(kt_, lq, hi, kb, t), qf[t], s[kb], 0, 0, 0);
+          dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(vt_, lq, hi, kb, t), df[t], dp[kb], 0, 0, 0);
+        }
+      }
+      // element j of block kb is key key0 + 32kb + 8(j/4) + 4hi + j%4 of this lane's query
+      long long bound = lim_abs - key0;
+      bound = bound < 0 ? 0 : (bound > kTile ? kTile : bound);
+      const int bnd = (int)bound - 4 * hi;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          float p = __builtin_amdgcn_exp2f(s[kb][j] * a.scale_log2 - Lc);
+          if (need_mask && kb * 32 + (j >> 2) * 8 + (j & 3) >= bnd) p = 0.f;
+          s[kb][j] = p * (dp[kb][j] - Dl);  // dS^T
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 dsb = pack8(s[ks >> 1], ks & 1);
+#pragma unroll
+        for (int db = 0; db < kDBlocks; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(kt_, lane, ks, db), dsb, acc[db], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's share of tile kt+1 has landed in LDS
+    __syncthreads();
+  }
+  if (qrow < a.Sq) {
+    float* dqrow = a.dq + ((int64_t)b * a.Sq + qrow) * rs + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        f32x4* p = (f32x4*)(dqrow + 32 * db + 8 * jg + 4 * hi);
+        f32x4 x = *p;
+        x += f32x4{acc[db][4 * jg], acc[db][4 * jg + 1], acc[db][4 * jg + 2], acc[db][4 * jg + 3]} * a.scale;
+        *p = x;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dk, dv: 128 keys per workgroup, 64-query tiles.
+template <int D>
+__global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(KArgs a) {
+  constexpr int kDSteps = D / 16, kDBlocks = D / 32, kTileBytes = kTile * D * 2;
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];  // Q[0], Q[1], dO[0], dO[1]
+  __shared__ __attribute__((aligned(16))) float lt[2][kTile], dt[2][kTile];  // lse*log2(e) (+inf: P = 0), Delta
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, lq = lane & 31, hi = lane >> 5;
+  const int BH = a.B * a.H;
+  const int kblk = (int)(blockIdx.x / BH);  // ascending: the earliest keys are seen by the most queries
+  const int bh = (int)(blockIdx.x % BH);
+  const int b = bh / a.H, h = bh % a.H;
+  const int64_t rs = (int64_t)a.H * D;
+  const int kv_lim = clamp_kv(a.kv_len, b, a.Sk);
+  const int key_first = kblk * kBlockRows;
+  if (key_first >= kv_lim) return;  // only padding keys: seen by no query (uniform per workgroup)
+  long long q_begin = 0;           // first query that sees any key of this workgroup
+  if (a.causal) {
+    const long long f = a.k_pos0 + key_first - a.q_pos0;
+    q_begin = f < 0 ? 0 : f;
+  }
+  const int qt0 = (int)(q_begin / kTile);
+  const int n_qt = (a.Sq + kTile - 1) / kTile;
+
+  const int k0 = key_first + wave * kRowsPerWave;
+  const __bf16* kbase = a.k + (int64_t)b * a.Sk * rs + (int64_t)h * D;
+  const __bf16* vbase = a.v + (int64_t)b * a.Sk * rs + (int64_t)h * D;
+  bf16x8 kf[kDSteps], vf[kDSteps];
+  load_rows<D>(kf, kbase, rs, k0, kv_lim, lq, hi);
+  load_rows<D>(vf, vbase, rs, k0, kv_lim, lq, hi);
+  const int key = k0 + lq;
+  const bool key_live = key < kv_lim;
+  // causal: query index i sees this lane's key iff i >= qmin
+  long long qmin = 0;
+  if (a.causal) qmin = a.k_pos0 + key - a.q_pos0;
+
+  TileCopy<D> cp;
+  cp.init(wave, lane, (uint32_t)(rs * 2));
+  const __bf16* qbase = a.q + (int64_t)b * a.Sq * rs + (int64_t)h * D;
+  const __bf16* dbase = a.dout + (int64_t)b * a.Sq * rs + (int64_t)h * D;
+  char* const qbuf = smem;
+  char* const dbuf = smem + 2 * kTileBytes;
+  auto stats = [&](int t, int slot) {  // lse and Delta of the 64 rows of query tile t
+    if (tid < kTile) {
+      const int r = t * kTile + tid;
+      float L = INFINITY, Dv = 0.f;
+      if (r < a.Sq) {
+        const float l = a.lse[(int64_t)bh * a.Sq + r];
+        L = l == -INFINITY ? INFINITY : l * kLog2e;
+        Dv = a.delta[(int64_t)bh * a.Sq + r];
+      }
+      lt[slot][tid] = L;
+      dt[slot][tid] = Dv;
+    }
+  };
+
+  f32x16 acck[kDBlocks], accv[kDBlocks];
+#pragma unroll
+  for (int i = 0; i < kDBlocks; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acck[i][j] = accv[i][j] = 0.f;
+
+  if (qt0 < n_qt) {
+    cp.copy(qbase, rs, qt0 * kTile, a.Sq, qbuf, wave);
+    cp.copy(dbase, rs, qt0 * kTile, a.Sq, dbuf, wave);
+    stats(qt0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = qt0; t < n_qt; ++t) {
+    const int buf = (t - qt0) & 1;
+    if (t + 1 < n_qt) {
+      cp.copy(qbase, rs, (t + 1) * kTile, a.Sq, qbuf + (buf ^ 1) * kTileBytes, wave);
+      cp.copy(dbase, rs, (t + 1) * kTile, a.Sq, dbuf + (buf ^ 1) * kTileBytes, wave);
+      stats(t + 1, buf ^ 1);
+    }
+    const int qt0_row = t * kTile;
+    bool skip = k0 >= kv_lim;
+    bool need_mask = false;
+    if (a.causal) {
+      // wave keys k0 .. k0+31 are seen by queries >= k_pos0 + key - q_pos0
+      if ((long long)qt0_row + kTile - 1 < a.k_pos0 + k0 - a.q_pos0) skip = true;
+      if ((long long)qt0_row < a.k_pos0 + k0 + kRowsPerWave - 1 - a.q_pos0) need_mask = true;
+    }
+    if (!skip) {
+      const char* qt_ = qbuf + buf * kTileBytes;
+      const char* dt_ = dbuf + buf * kTileBytes;
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) s[qb][j] = dp[qb][j] = 0.f;
+#pragma unroll
+        for (int d = 0; d < kDSteps; ++d) {
+          s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qt_, lq, hi, qb, d), kf[d], s[qb], 0, 0, 0);
+          dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(dt_, lq, hi, qb, d), vf[d], dp[qb], 0, 0, 0);
+        }
+      }
+      // element j of block qb is query qt0_row + 32qb + 8(j/4) + 4hi + j%4 against this lane's key
+      long long thr = qmin - qt0_row - 4 * hi;  // hidden iff 32qb + 8(j/4) + j%4 < thr
+      thr = thr < -1 ? -1 : (thr > 2 * kTile ? 2 * kTile : thr);
+      const int ithr = (int)thr;
+      f32x16 p[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 L4 = *(const f32x4*)&lt[buf][qb * 32 + 8 * g + 4 * hi];
+          const f32x4 D4 = *(const f32x4*)&dt[buf][qb * 32 + 8 * g + 4 * hi];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int j = 4 * g + jj;
+            float pv = __builtin_amdgcn_exp2f(s[qb][j] * a.scale_log2 - L4[jj]);
+            if (!key_live || (need_mask && qb * 32 + 8 * g + jj < ithr)) pv = 0.f;
+            p[qb][j] = pv;
+            s[qb][j] = pv * (dp[qb][j] - D4[jj]);  // dS
+          }
+        }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 pb = pack8(p[ks >> 1], ks & 1);
+        const bf16x8 dsb = pack8(s[ks >> 1], ks & 1);
+#pragma unroll
+        for (int db = 0; db < kDBlocks; ++db) {
+          accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(dt_, lane, ks, db), pb, accv[db], 0, 0, 0);
+          acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qt_, lane, ks, db), dsb, acck[db], 0, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+  if (key < a.Sk) {
+    float* dkrow = a.dk + ((int64_t)b * a.Sk + key) * rs + (int64_t)h * D;
+    float* dvrow = a.dv + ((int64_t)b * a.Sk + key) * rs + (int64_t)h * D;
+#pragma unroll
+    for (int db = 0; db < kDBlocks; ++db)
+#pragma unroll
+      for (int jg = 0; jg < 4; ++jg) {
+        const int d0 = 32 * db + 8 * jg + 4 * hi;
+        f32x4 x = *(f32x4*)(dkrow + d0);
+        x += f32x4{acck[db][4 * jg], acck[db][4 * jg + 1], acck[db][4 * jg + 2], acck[db][4 * jg + 3]} * a.scale;
+        *(f32x4*)(dkrow + d0) = x;
+        f32x4 y = *(f32x4*)(dvrow + d0);
+        y += f32x4{accv[db][4 * jg], accv[db][4 * jg + 1], accv[db][4 * jg + 2], accv[db][4 * jg + 3]};
+        *(f32x4*)(dvrow + d0) = y;
+      }
+  }
+}
+
+template <int D>
+hipError_t launch_d(const AttnBwdArgs& x, hipStream_t st) {
+  KArgs a;
+  a.q = (const __bf16*)x.q, a.k = (const __bf16*)x.k, a.v = (const __bf16*)x.v, a.dout = (const __bf16*)x.dout;
+  a.lse = x.lse, a.delta = x.delta, a.dq = x.dq, a.dk = x.dk, a.dv = x.dv, a.kv_len = x.kv_len;
+  a.B = x.B, a.Sq = x.Sq, a.Sk = x.Sk, a.H = x.H;
+  a.causal = x.causal ? 1 : 0;
+  a.q_pos0 = x.q_pos0, a.k_pos0 = x.k_pos0;
+  a.scale = x.scale, a.scale_log2 = x.scale * kLog2e;
+  const int64_t BH = (int64_t)x.B * x.H;
+  const int64_t qblocks = (int64_t)((x.Sq + kBlockRows - 1) / kBlockRows) * BH;
+  const int64_t kblocks = (int64_t)((x.Sk + kBlockRows - 1) / kBlockRows) * BH;
+  if (qblocks > 0x7fffffff || kblocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)qblocks), dim3(kThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)kblocks), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t st) {
+  if (a.D == 128) return launch_d<128>(a, st);
+  if (a.D == 64) return launch_d<64>(a, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tha

@@ -31,6 +31,24 @@ struct AttnArgs {
   float scale;
 };
 
+struct AttnBwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* delta;  // [B,H,Sq] workspace
+  const int* kv_len;
+  int B, Sq, Sk, H, D;
+  bool causal;
+  long long q_pos0, k_pos0;
+  float scale;
+};
+
 hipError_t launch_shard_permute(const ShardPtrs& shards, int P, int group, void* out, int B, int S, int H, int D,
                                 int elem_bytes, hipStream_t stream);
 hipError_t launch_shard_unpermute(const void* in, int P, int group, const ShardPtrs& shards, int B, int S, int H,
@@ -42,5 +60,8 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_bf16_d128(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_bf16_d128_wide(const AttnArgs& a, hipStream_t stream);
 int64_t attn_bf16_d128_wide_blocks(const AttnArgs& a);
+hipError_t launch_attn_bwd_delta(const AttnBwdArgs& a, int in_dt, hipStream_t stream);
+hipError_t launch_attn_bwd_f32(const AttnBwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_bwd_bf16(const AttnBwdArgs& a, hipStream_t stream);
 
 }  // namespace tha

@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_symbols()
-    assert {"attn_fwd", "attn_merge_lse", "shard_permute", "shard_unpermute", "tha_status_string",
+    assert {"attn_fwd", "attn_bwd", "attn_merge_lse", "shard_permute", "shard_unpermute", "tha_status_string",
             "tha_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -82,6 +82,28 @@ def test_attn_fwd_validation(lib):
     assert _attn(lib, D=96) == U                         # bf16 path: D in {64, 128}
     assert _attn(lib, in_dt=0, D=257) == U               # fp32 path: D <= 256
     assert _attn(lib, H=1 << 20, D=128) == U             # token row too long for 32-bit tile offsets
+
+
+def _bwd(lib, q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, ws=P, B=1, Sq=8, Sk=8, H=1, D=128, in_dt=1,
+         flags=0, qp=0, kp=0, kv=None, scale=0.088, stream=None):
+    return lib.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, B, Sq, Sk, H, D, in_dt, flags, qp, kp, kv, scale, stream)
+
+
+def test_attn_bwd_validation(lib):
+    E, U = T.THA_ERR_INVALID, T.THA_ERR_UNSUPPORTED
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv", "ws"):
+        assert _bwd(lib, **{name: None}) == E, name
+    for kw in ("B", "Sq", "Sk", "H", "D"):
+        assert _bwd(lib, **{kw: 0}) == E
+    assert _bwd(lib, flags=4) == E
+    assert _bwd(lib, flags=T.THA_MASK_KEY_PADDING) == E
+    assert _bwd(lib, scale=float("nan")) == E
+    assert _bwd(lib, scale=0.0) == E
+    assert _bwd(lib, qp=1 << 62) == E
+    assert _bwd(lib, in_dt=3) == U
+    assert _bwd(lib, D=96) == U
+    assert _bwd(lib, in_dt=0, D=300) == U
+    assert _bwd(lib, H=1 << 20, D=128) == U
 
 
 def _ptr_arr(n, val=0x1000):
