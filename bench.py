@@ -180,6 +180,7 @@ def main():
     del cp_src, cp_dst
 
     if not args.no_side:
+        components.update(bwd_side(T, W, torch, dev, grouped, out, lse, S, Hl, D, flops, args.seed))
         components.update(ring_side(T, W, torch, dev, args.seed))
         components.update(merge_rotating(T, torch, dev))
 
@@ -242,6 +243,29 @@ def gpu_busy(torch, ms=30.0):
     are all enqueued before the GPU reaches them: their event intervals then hold GPU time only,
     not the host's per-call launch overhead."""
     torch.cuda._sleep(int(ms * 1e-3 * 2.0e9))
+
+
+def bwd_side(T, W, torch, dev, grouped, out, lse, S, H, D, fwd_flops, seed):
+    """attn_bwd at the Ulysses share's attention (causal S=32768, 8 heads x 128): gradients of
+    the step's own forward output for a seeded dout.  Algorithmic work: 5 products of 2*D FLOP
+    per visible pair (S, dP, dV, dK, dQ), i.e. 2.5x the forward's."""
+    dout = W.randn((1, S, H, D), W.generator(seed + 7), torch.bfloat16).to(dev)
+    dq = torch.zeros((1, S, H, D), dtype=torch.float32, device=dev)
+    dk, dv = torch.zeros_like(dq), torch.zeros_like(dq)
+    ws = torch.empty((H * S,), dtype=torch.float32, device=dev)
+    q, k, v = grouped["q"], grouped["k"], grouped["v"]
+
+    def call(i):
+        T.attn_bwd(q, k, v, out, dout, lse, causal=True, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    per = batch_times(torch, call, batches=3, n=3)
+    ms = per[len(per) // 2]
+    flops = 2.5 * fwd_flops
+    return {"attn_bwd": {"ms_per_call": ms, "ms_min": per[0], "flop_per_call": flops,
+                         "TFLOP_per_s": flops / (ms * 1e-3) / 1e12,
+                         "frac_mfma_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                         "timing": "median over 3 batches of 3 back-to-back calls (Delta pre-pass, dq and "
+                                   "dk/dv kernels), one event pair per batch"}}
 
 
 def ring_side(T, W, torch, dev, seed):
