@@ -59,8 +59,9 @@ enum { THA_F32 = 0, THA_BF16 = 1 };
 enum {
   THA_MASK_NONE = 0,
   THA_MASK_CAUSAL = 1,     /* key visible iff k_pos0 + j <= q_pos0 + i ("adv07: Sequence Parallel", Q4) */
-  THA_MASK_KEY_PADDING = 2 /* key j of sequence b visible iff j < kv_len[b] ("Support deepspeed
-                              sequence parallel": the mask is 'token is not padding') */
+  THA_MASK_KEY_PADDING = 2, /* key j of sequence b visible iff j < kv_len[b] ("Support deepspeed
+                               sequence parallel": the mask is 'token is not padding') */
+  THA_ACCUMULATE = 4         /* attn_fwd_ex only: merge into the running (o, lse), see there */
 };
 
 /* Largest pointer arrays accepted by attn_merge_lse and the permutes. */
@@ -103,6 +104,35 @@ enum {
 THA_API int attn_fwd(const void* q, const void* k, const void* v, void* o, int out_dt, float* lse, int B, int Sq,
              int Sk, int H, int D, int in_dt, unsigned mask_flags, long long q_pos0, long long k_pos0,
              const int* kv_len, float scale, void* stream);
+
+/*
+ * attn_fwd_ex -- attn_fwd with explicit tensor strides and an optional fused Ring step.
+ *
+ * strides: NULL (contiguous [B,S,H,D] tensors, as attn_fwd) or 8 element strides
+ *   { q_batch, q_token, k_batch, k_token, v_batch, v_token, o_batch, o_token }:
+ *   element (b, s, h, d) of q lives at q[b*q_batch + s*q_token + h*D + d], and likewise for k,
+ *   v and o (heads contiguous at stride D inside a token, dims contiguous).  This takes the
+ *   packed-QKV layout [B,S,3,H,D] ("Megatron-LM ..." notes and "关于数据分割和合并": separate or
+ *   packed Q/K/V inputs) as three views (token stride 3*H*D) and head-subset views of a wider
+ *   tensor (token stride H_total*D) without copies.  Requirements: every token stride >= H*D and
+ *   <= 2^24; with B > 1 every batch stride >= (tokens of that tensor) * token stride (no
+ *   overlap); k_token == v_token (THA_ERR_UNSUPPORTED otherwise); on the bf16 path q, k, v
+ *   16-byte aligned with strides multiples of 8 elements, o 8-byte (bf16) or 16-byte (fp32)
+ *   aligned with strides multiples of 4 elements (THA_ERR_UNSUPPORTED otherwise).
+ *
+ * flags: the mask flags of attn_fwd, plus THA_ACCUMULATE.  With THA_ACCUMULATE, o (out_dt must
+ *   be THA_F32) and lse (required) hold a running result over other keys, and this call merges
+ *   its own result into them in place by the log-sum-exp rule of attn_merge_lse (the Ring step
+ *   that accumulates block results into the full attention, "adv07: Sequence Parallel" Q5),
+ *   with no separate partial buffers or merge pass.  A row whose running lse is -inf counts as
+ *   having no keys yet: its o is not read (so a Ring pass may start from lse = -inf and any o).
+ *   Calls that overlap on the same rows of o / lse race.
+ * Other arguments, results and errors as attn_fwd; THA_ERR_INVALID also for THA_ACCUMULATE
+ * with a bf16 o or a null lse.
+ */
+THA_API int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int out_dt, float* lse, int B, int Sq,
+                int Sk, int H, int D, int in_dt, unsigned flags, long long q_pos0, long long k_pos0,
+                const int* kv_len, float scale, const long long* strides, void* stream);
 
 /*
  * attn_bwd -- gradients of attn_fwd with respect to q, k and v for the cotangent

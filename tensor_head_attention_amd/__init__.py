@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_PKG, "libtha.so")
 THA_OK, THA_ERR_INVALID, THA_ERR_UNSUPPORTED, THA_ERR_HIP = 0, -1, -2, -3
 THA_F32, THA_BF16 = 0, 1
 THA_MASK_NONE, THA_MASK_CAUSAL, THA_MASK_KEY_PADDING = 0, 1, 2
+THA_ACCUMULATE = 4
 THA_MAX_PARTS = THA_MAX_SHARDS = 64
 
 _lib = None
@@ -42,12 +43,14 @@ def load_library(path: str = LIB_PATH):
     vp, ci, cll = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, ci, vp, ci, ci, ci, ci, ci, ci, ctypes.c_uint, cll, cll, vp,
                              ctypes.c_float, vp]
+    lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, ci, vp, ci, ci, ci, ci, ci, ci, ctypes.c_uint, cll, cll, vp,
+                                ctypes.c_float, vp, vp]
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_uint, cll, cll,
                              vp, ctypes.c_float, vp]
     lib.attn_merge_lse.argtypes = [ci, vp, vp, ci, vp, ci, vp, ci, ci, ci, ci, vp]
     lib.shard_permute.argtypes = [vp, ci, ci, vp, ci, ci, ci, ci, ci, vp]
     lib.shard_unpermute.argtypes = [vp, ci, ci, vp, ci, ci, ci, ci, ci, vp]
-    for f in (lib.attn_fwd, lib.attn_bwd, lib.attn_merge_lse, lib.shard_permute, lib.shard_unpermute,
+    for f in (lib.attn_fwd, lib.attn_fwd_ex, lib.attn_bwd, lib.attn_merge_lse, lib.shard_permute, lib.shard_unpermute,
               lib.tha_version):
         f.restype = ci
     lib.tha_status_string.argtypes = [ci]
@@ -128,6 +131,57 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool 
                        int(q_pos0), int(k_pos0), kvp, float(scale), _stream(q))
     _check(rc, "attn_fwd")
     return (out, lse) if return_lse else out
+
+
+def _view_strides(t: torch.Tensor, name: str):
+    """(batch, token) element strides of a [B, S, H, D] view with heads and dims contiguous."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != 4 or t.stride(3) != 1 or t.stride(2) != t.shape[3]:
+        raise ValueError(f"{name} must be a [B, S, H, D] view with contiguous heads and dims")
+    return t.stride(0), t.stride(1)
+
+
+def attn_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+                kv_len: Optional[torch.Tensor] = None, q_pos0: int = 0, k_pos0: int = 0,
+                scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
+                out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                accumulate: bool = False):
+    """attn_fwd on strided views (e.g. packed QKV [B,S,3,H,D] split into q, k, v; head subsets),
+    and with accumulate=True the fused Ring step: out (fp32) and lse hold a running result over
+    other keys and this call merges its own result into them (see tha.h attn_fwd_ex).
+    Returns (out, lse)."""
+    load_library()
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate needs the running out and lse")
+        out = torch.empty((B, Sq, H, D), dtype=out_dtype or q.dtype, device=q.device)
+    if lse is None:
+        if accumulate:
+            raise ValueError("accumulate needs the running out and lse")
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
+    _dev(lse, "lse")
+    strides = []
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        strides += list(_view_strides(t, n))
+    st = (ctypes.c_longlong * 8)(*strides)
+    flags = (THA_MASK_CAUSAL if causal else 0) | (THA_ACCUMULATE if accumulate else 0)
+    kvp = None
+    if kv_len is not None:
+        kv_len = _dev(kv_len, "kv_len")
+        if kv_len.dtype != torch.int32:
+            raise ValueError("kv_len must be int32")
+        flags |= THA_MASK_KEY_PADDING
+        kvp = kv_len.data_ptr()
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rc = _lib.attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dt(out.dtype), lse.data_ptr(),
+                          B, Sq, Sk, H, D, _dt(q.dtype), flags, int(q_pos0), int(k_pos0), kvp, float(scale), st,
+                          _stream(q))
+    _check(rc, "attn_fwd_ex")
+    return out, lse
 
 
 def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,

@@ -47,29 +47,76 @@ const char* tha_status_string(int status) {
   }
 }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, int out_dt, float* lse, int B, int Sq, int Sk,
-             int H, int D, int in_dt, unsigned mask_flags, long long q_pos0, long long k_pos0, const int* kv_len,
-             float scale, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of attn_fwd and attn_fwd_ex; st8: {q_bs, q_rs, k_bs, k_rs, v_bs, v_rs, o_bs, o_rs}.
+int fwd_common(const void* q, const void* k, const void* v, void* o, int out_dt, float* lse, int B, int Sq, int Sk,
+               int H, int D, int in_dt, unsigned flags, long long q_pos0, long long k_pos0, const int* kv_len,
+               float scale, const long long* st8, void* stream) {
   if (!q || !k || !v || !o) return THA_ERR_INVALID;
   if (B <= 0 || Sq <= 0 || Sk <= 0 || H <= 0 || D <= 0) return THA_ERR_INVALID;
-  if (mask_flags & ~(unsigned)(THA_MASK_CAUSAL | THA_MASK_KEY_PADDING)) return THA_ERR_INVALID;
-  if ((mask_flags & THA_MASK_KEY_PADDING) && !kv_len) return THA_ERR_INVALID;
+  if (flags & ~(unsigned)(THA_MASK_CAUSAL | THA_MASK_KEY_PADDING | THA_ACCUMULATE)) return THA_ERR_INVALID;
+  if ((flags & THA_MASK_KEY_PADDING) && !kv_len) return THA_ERR_INVALID;
   if (!isfinite(scale) || !(scale > 0.f)) return THA_ERR_INVALID;
   if (q_pos0 >= kMaxPos || q_pos0 <= -kMaxPos || k_pos0 >= kMaxPos || k_pos0 <= -kMaxPos) return THA_ERR_INVALID;
+  const bool accumulate = (flags & THA_ACCUMULATE) != 0;
+  if (accumulate && (out_dt != THA_F32 || !lse)) return THA_ERR_INVALID;
   if (!dtype_ok(in_dt) || !dtype_ok(out_dt)) return THA_ERR_UNSUPPORTED;
   if ((int64_t)H * D > kMaxRowElems) return THA_ERR_UNSUPPORTED;
   if (in_dt == THA_BF16 && D != 128 && D != 64) return THA_ERR_UNSUPPORTED;
   if (in_dt == THA_F32 && D > 256) return THA_ERR_UNSUPPORTED;
+  const int64_t hd = (int64_t)H * D;
+  const int64_t rows[4] = {Sq, Sk, Sk, Sq};
+  for (int t = 0; t < 4; ++t) {
+    const int64_t bs = st8[2 * t], rs = st8[2 * t + 1];
+    if (rs < hd || rs > kMaxRowElems || bs < 0) return THA_ERR_INVALID;
+    if (B > 1 && bs < rows[t] * rs) return THA_ERR_INVALID;  // batches must not overlap
+  }
+  if (st8[3] != st8[5]) return THA_ERR_UNSUPPORTED;  // k and v share one token stride
+  if (in_dt == THA_BF16) {  // 16-byte vector accesses of q, k, v; 4-element vectors of o
+    for (int t = 0; t < 3; ++t)
+      if (st8[2 * t] % 8 || st8[2 * t + 1] % 8) return THA_ERR_UNSUPPORTED;
+    if ((uintptr_t)q % 16 || (uintptr_t)k % 16 || (uintptr_t)v % 16) return THA_ERR_UNSUPPORTED;
+    if (st8[6] % 4 || st8[7] % 4 || (uintptr_t)o % (out_dt == THA_BF16 ? 8 : 16)) return THA_ERR_UNSUPPORTED;
+  }
   tha::AttnArgs a;
   a.q = q, a.k = k, a.v = v, a.o = o, a.lse = lse;
-  a.kv_len = (mask_flags & THA_MASK_KEY_PADDING) ? kv_len : nullptr;
+  a.kv_len = (flags & THA_MASK_KEY_PADDING) ? kv_len : nullptr;
   a.B = B, a.Sq = Sq, a.Sk = Sk, a.H = H, a.D = D;
   a.out_dt = out_dt;
-  a.causal = (mask_flags & THA_MASK_CAUSAL) != 0;
+  a.causal = (flags & THA_MASK_CAUSAL) != 0;
   a.q_pos0 = q_pos0, a.k_pos0 = k_pos0;
   a.scale = scale;
-  hipStream_t st = (hipStream_t)stream;
-  return hip_status(in_dt == THA_BF16 ? tha::launch_attn_bf16(a, st) : tha::launch_attn_f32(a, st));
+  a.q_bs = st8[0], a.q_rs = st8[1], a.k_bs = st8[2], a.k_rs = st8[3];
+  a.v_bs = st8[4], a.v_rs = st8[5], a.o_bs = st8[6], a.o_rs = st8[7];
+  a.accumulate = accumulate;
+  hipStream_t s = (hipStream_t)stream;
+  return hip_status(in_dt == THA_BF16 ? tha::launch_attn_bf16(a, s) : tha::launch_attn_f32(a, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, int out_dt, float* lse, int B, int Sq, int Sk,
+             int H, int D, int in_dt, unsigned mask_flags, long long q_pos0, long long k_pos0, const int* kv_len,
+             float scale, void* stream) {
+  if (mask_flags & THA_ACCUMULATE) return THA_ERR_INVALID;  // attn_fwd_ex only
+  const long long hd = (long long)H * D;
+  const long long st8[8] = {Sq * hd, hd, Sk * hd, hd, Sk * hd, hd, Sq * hd, hd};
+  return fwd_common(q, k, v, o, out_dt, lse, B, Sq, Sk, H, D, in_dt, mask_flags, q_pos0, k_pos0, kv_len, scale, st8,
+                    stream);
+}
+
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int out_dt, float* lse, int B, int Sq, int Sk,
+                int H, int D, int in_dt, unsigned flags, long long q_pos0, long long k_pos0, const int* kv_len,
+                float scale, const long long* strides, void* stream) {
+  const long long hd = (long long)H * D;
+  const long long dflt[8] = {Sq * hd, hd, Sk * hd, hd, Sk * hd, hd, Sq * hd, hd};
+  return fwd_common(q, k, v, o, out_dt, lse, B, Sq, Sk, H, D, in_dt, flags, q_pos0, k_pos0, kv_len, scale,
+                    strides ? strides : dflt, stream);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, float* dq,

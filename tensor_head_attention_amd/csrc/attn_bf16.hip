@@ -42,6 +42,7 @@
 #include <cstdlib>
 #include <cstring>
 
+#include "attn_epilogue.h"
 #include "device_common.h"
 #include "tha_kernels.h"
 
@@ -86,6 +87,8 @@ struct KernelArgs {
   float scale;       // natural-log scale (for lse)
   float scale_log2;  // scale * log2(e)
   float rescale_raw; // kRescaleLog2 / scale_log2: raw-score growth that triggers a rescale
+  int64_t q_bs, q_rs, k_bs, k_rs, v_bs, o_bs, o_rs;  // element strides (batch, token); v_rs == k_rs
+  int accumulate;
 };
 
 template <int D, typename OutT>
@@ -108,8 +111,9 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(KernelArgs a) {
   const int qt = n_qt - 1 - (int)(blockIdx.x / BH);  // heaviest causal tiles first
   const int bh = (int)(blockIdx.x % BH);
   const int b = bh / a.H, h = bh % a.H;
-  const int64_t row_stride = (int64_t)a.H * D;     // elements between consecutive tokens
+  const int64_t row_stride = a.k_rs;                // K/V elements between consecutive tokens
   const uint32_t row_bytes = (uint32_t)(row_stride * 2);
+  const uint32_t q_row_bytes = (uint32_t)(a.q_rs * 2);
 
   // Visible key range of the workgroup.
   int kv_lim = a.Sk;
@@ -132,15 +136,15 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(KernelArgs a) {
   bf16x8 qf[kDSteps];
   {
     const int rows_valid = max(0, min(kRowsPerWave, a.Sq - q0));
-    const __bf16* qbase = a.q + (((int64_t)b * a.Sq + min(q0, a.Sq - 1)) * a.H + h) * D;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase, (uint32_t)rows_valid * row_bytes);
+    const __bf16* qbase = a.q + (int64_t)b * a.q_bs + (int64_t)min(q0, a.Sq - 1) * a.q_rs + (int64_t)h * D;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qbase, (uint32_t)rows_valid * q_row_bytes);
 #pragma unroll
     for (int t = 0; t < kDSteps; ++t)
-      qf[t] = __builtin_bit_cast(bf16x8, buffer_load_16(rq, (uint32_t)lq * row_bytes + (uint32_t)(16 * t + 8 * hi) * 2));
+      qf[t] = __builtin_bit_cast(bf16x8, buffer_load_16(rq, (uint32_t)lq * q_row_bytes + (uint32_t)(16 * t + 8 * hi) * 2));
   }
 
-  const __bf16* kbase = a.k + ((int64_t)b * a.Sk * a.H + h) * D;
-  const __bf16* vbase = a.v + ((int64_t)b * a.Sk * a.H + h) * D;
+  const __bf16* kbase = a.k + (int64_t)b * a.k_bs + (int64_t)h * D;
+  const __bf16* vbase = a.v + (int64_t)b * a.v_bs + (int64_t)h * D;
 
   // Per-lane global offsets of this wave's share of a tile copy: wave-wide load u fills
   // LDS bytes [(wave*kLoadsPerWave + u) * 1024, +1024), lane i its 16 bytes at i*16, i.e.
@@ -298,27 +302,11 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(KernelArgs a) {
   // ---- epilogue ---------------------------------------------------------------
   if (!wave_live) return;
   const float l_tot = sum_across_halves(l_run);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
   const int qrow = q0 + lq;
   if (qrow < a.Sq) {
-    OutT* orow = (OutT*)a.o + (((int64_t)b * a.Sq + qrow) * a.H + h) * D;
-#pragma unroll
-    for (int db = 0; db < kDBlocks; ++db)
-#pragma unroll
-      for (int jg = 0; jg < 4; ++jg) {
-        const int d0 = 32 * db + 8 * jg + 4 * hi;
-        if constexpr (sizeof(OutT) == 2) {
-          bf16x4 r = {(__bf16)(o_acc[db][4 * jg] * inv), (__bf16)(o_acc[db][4 * jg + 1] * inv),
-                      (__bf16)(o_acc[db][4 * jg + 2] * inv), (__bf16)(o_acc[db][4 * jg + 3] * inv)};
-          *(bf16x4*)(orow + d0) = r;
-        } else {
-          f32x4 r = {o_acc[db][4 * jg] * inv, o_acc[db][4 * jg + 1] * inv, o_acc[db][4 * jg + 2] * inv,
-                     o_acc[db][4 * jg + 3] * inv};
-          *(f32x4*)(orow + d0) = r;
-        }
-      }
-    if (a.lse && hi == 0)
-      a.lse[((int64_t)b * a.H + h) * a.Sq + qrow] = l_tot > 0.f ? m_run * a.scale + logf(l_tot) : -INFINITY;
+    OutT* orow = (OutT*)a.o + (int64_t)b * a.o_bs + (int64_t)qrow * a.o_rs + (int64_t)h * D;
+    float* lse_p = a.lse ? a.lse + ((int64_t)b * a.H + h) * a.Sq + qrow : nullptr;
+    store_row<kDBlocks>(o_acc, orow, lse_p, hi, l_tot, m_run, a.scale, a.accumulate != 0);
   }
 }
 
@@ -337,6 +325,8 @@ hipError_t launch_d(const AttnArgs& x, hipStream_t st) {
   a.scale = x.scale;
   a.scale_log2 = x.scale * kLog2e;
   a.rescale_raw = kRescaleLog2 / a.scale_log2;
+  a.q_bs = x.q_bs, a.q_rs = x.q_rs, a.k_bs = x.k_bs, a.k_rs = x.k_rs, a.v_bs = x.v_bs;
+  a.o_bs = x.o_bs, a.o_rs = x.o_rs, a.accumulate = x.accumulate ? 1 : 0;
   const int64_t n_qt = (x.Sq + kBlockM - 1) / kBlockM;
   const int64_t blocks = n_qt * x.B * x.H;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;

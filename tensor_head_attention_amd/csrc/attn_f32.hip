@@ -32,12 +32,17 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+struct F32Strides {
+  int64_t q_bs, q_rs, k_bs, k_rs, v_bs, o_bs, o_rs;  // elements (batch, token); v_rs == k_rs
+};
+
 template <typename OutT>
 __global__ void __launch_bounds__(kWaves * 64) attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                                const float* __restrict__ v, OutT* __restrict__ o,
                                                                float* __restrict__ lse, const int* __restrict__ kv_len,
                                                                int B, int Sq, int Sk, int H, int D, int causal,
-                                                               long long q_pos0, long long k_pos0, float scale) {
+                                                               long long q_pos0, long long k_pos0, float scale,
+                                                               F32Strides st, int accumulate) {
   __shared__ float qs[kWaves][kMaxD];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t row_id = (int64_t)blockIdx.x * kWaves + wave;
@@ -46,10 +51,10 @@ __global__ void __launch_bounds__(kWaves * 64) attn_f32_kernel(const float* __re
   const int64_t bh = row_id / Sq;
   const int h = (int)(bh % H);
   const int b = (int)(bh / H);
-  const int64_t rs = (int64_t)H * D;  // row stride in elements
-  const float* qrow = q + ((int64_t)b * Sq + i) * rs + (int64_t)h * D;
-  const float* kb = k + (int64_t)b * Sk * rs + (int64_t)h * D;
-  const float* vb = v + (int64_t)b * Sk * rs + (int64_t)h * D;
+  const int64_t rs = st.k_rs;  // K/V elements between consecutive tokens
+  const float* qrow = q + (int64_t)b * st.q_bs + (int64_t)i * st.q_rs + (int64_t)h * D;
+  const float* kb = k + (int64_t)b * st.k_bs + (int64_t)h * D;
+  const float* vb = v + (int64_t)b * st.v_bs + (int64_t)h * D;
   for (int d = lane; d < D; d += 64) qs[wave][d] = qrow[d];
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -97,14 +102,28 @@ __global__ void __launch_bounds__(kWaves * 64) attn_f32_kernel(const float* __re
     }
     m = m_new;
   }
-  OutT* orow = o + ((int64_t)b * Sq + i) * rs + (int64_t)h * D;
+  OutT* orow = o + (int64_t)b * st.o_bs + (int64_t)i * st.o_rs + (int64_t)h * D;
   const float inv = l > 0.f ? 1.0f / l : 0.f;
+  const float lse_c = l > 0.f ? m + logf(l) : -INFINITY;
+  float* lse_p = lse ? lse + ((int64_t)b * H + h) * Sq + i : nullptr;
+  if constexpr (sizeof(OutT) == 4) {
+    if (accumulate) {  // merge into the running result (every lane reads lse before lane 0 writes it)
+      const MergeW w = merge_weights(*lse_p, lse_c);
+#pragma unroll
+      for (int r = 0; r < kMaxD / 64; ++r) {
+        const int d = lane + 64 * r;
+        if (d < D) orow[d] = (w.a != 0.f ? w.a * (float)orow[d] : 0.f) + w.c * (acc[r] * inv);
+      }
+      if (lane == 0) *lse_p = w.lse;
+      return;
+    }
+  }
 #pragma unroll
   for (int r = 0; r < kMaxD / 64; ++r) {
     const int d = lane + 64 * r;
     if (d < D) orow[d] = (OutT)(acc[r] * inv);
   }
-  if (lse && lane == 0) lse[((int64_t)b * H + h) * Sq + i] = l > 0.f ? m + logf(l) : -INFINITY;
+  if (lse_p && lane == 0) *lse_p = lse_c;
 }
 
 }  // namespace
@@ -113,14 +132,15 @@ hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t st) {
   const int64_t rows = (int64_t)a.B * a.H * a.Sq;
   const int64_t blocks = (rows + kWaves - 1) / kWaves;
   if (blocks > 0x7fffffff || a.D > kMaxD) return hipErrorInvalidValue;
+  const F32Strides ss = {a.q_bs, a.q_rs, a.k_bs, a.k_rs, a.v_bs, a.o_bs, a.o_rs};
   if (a.out_dt == THA_F32)
     hipLaunchKernelGGL(attn_f32_kernel<float>, dim3((unsigned)blocks), dim3(kWaves * 64), 0, st, (const float*)a.q,
                        (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.kv_len, a.B, a.Sq, a.Sk, a.H, a.D,
-                       (int)a.causal, a.q_pos0, a.k_pos0, a.scale);
+                       (int)a.causal, a.q_pos0, a.k_pos0, a.scale, ss, a.accumulate ? 1 : 0);
   else
     hipLaunchKernelGGL(attn_f32_kernel<__bf16>, dim3((unsigned)blocks), dim3(kWaves * 64), 0, st, (const float*)a.q,
                        (const float*)a.k, (const float*)a.v, (__bf16*)a.o, a.lse, a.kv_len, a.B, a.Sq, a.Sk, a.H, a.D,
-                       (int)a.causal, a.q_pos0, a.k_pos0, a.scale);
+                       (int)a.causal, a.q_pos0, a.k_pos0, a.scale, ss, 0);
   return hipGetLastError();
 }
 

@@ -80,6 +80,21 @@ __device__ __forceinline__ float sum_across_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Weights that fold a chunk's attention result (o_c, lse_c) into a running one (o_r, lse_r) over
+// a disjoint key set, by the log-sum-exp rule of attn_merge_lse: o = a*o_r + c*o_c, lse = lse.
+// Neither side saw a key: a = c = 0, lse = -inf.  A chunk that saw no key gives a = 1, c = 0 and
+// lse = lse_r exactly.
+struct MergeW {
+  float a, c, lse;
+};
+__device__ __forceinline__ MergeW merge_weights(float lse_r, float lse_c) {
+  const float M = fmaxf(lse_r, lse_c);
+  if (M == -INFINITY) return {0.f, 0.f, -INFINITY};
+  const float wr = expf(lse_r - M), wc = expf(lse_c - M);
+  const float W = wr + wc;
+  return {wr / W, wc / W, M + logf(W)};
+}
+
 // Round-to-nearest-even fp32 -> bf16 pair (the hardware conversion on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16x2 v = {(__bf16)a, (__bf16)b};

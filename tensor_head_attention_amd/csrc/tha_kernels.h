@@ -29,6 +29,10 @@ struct AttnArgs {
   bool causal;
   long long q_pos0, k_pos0;
   float scale;
+  // element strides between batches (bs) and between tokens (rs); heads at stride D, dims at 1.
+  // k and v share one token stride (k_rs == v_rs).
+  int64_t q_bs, q_rs, k_bs, k_rs, v_bs, v_rs, o_bs, o_rs;
+  bool accumulate;  // o (fp32) and lse hold a running result: merge this call's result into them
 };
 
 struct AttnBwdArgs {

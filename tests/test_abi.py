@@ -30,7 +30,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_symbols()
-    assert {"attn_fwd", "attn_bwd", "attn_merge_lse", "shard_permute", "shard_unpermute", "tha_status_string",
+    assert {"attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_merge_lse", "shard_permute", "shard_unpermute", "tha_status_string",
             "tha_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -82,6 +82,36 @@ def test_attn_fwd_validation(lib):
     assert _attn(lib, D=96) == U                         # bf16 path: D in {64, 128}
     assert _attn(lib, in_dt=0, D=257) == U               # fp32 path: D <= 256
     assert _attn(lib, H=1 << 20, D=128) == U             # token row too long for 32-bit tile offsets
+
+
+def _fwdx(lib, q=P, k=P, v=P, o=P, out_dt=1, lse=P, B=2, Sq=8, Sk=8, H=1, D=128, in_dt=1, flags=0, qp=0, kp=0,
+          kv=None, scale=0.088, strides=None, stream=None):
+    st = (ctypes.c_longlong * 8)(*strides) if strides is not None else None
+    return lib.attn_fwd_ex(q, k, v, o, out_dt, lse, B, Sq, Sk, H, D, in_dt, flags, qp, kp, kv, scale, st, stream)
+
+
+def test_attn_fwd_ex_validation(lib):
+    E, U = T.THA_ERR_INVALID, T.THA_ERR_UNSUPPORTED
+    hd = 128
+    ok = [8 * 3 * hd, 3 * hd, 8 * 3 * hd, 3 * hd, 8 * 3 * hd, 3 * hd, 8 * hd, hd]  # packed QKV, contiguous o
+    assert _attn(lib, flags=T.THA_ACCUMULATE) == E                         # attn_fwd has no accumulate mode
+    assert _fwdx(lib, q=None, strides=ok) == E
+    assert _fwdx(lib, flags=T.THA_ACCUMULATE, out_dt=1, strides=ok) == E   # accumulate needs an fp32 o
+    assert _fwdx(lib, flags=T.THA_ACCUMULATE, out_dt=0, lse=None, strides=ok) == E  # ... and an lse
+    assert _fwdx(lib, flags=8, strides=ok) == E                             # unknown flag bit
+    bad = list(ok); bad[1] = hd - 8                                         # token stride < H*D
+    assert _fwdx(lib, strides=bad) == E
+    bad = list(ok); bad[0] = 3 * hd                                         # batches overlap
+    assert _fwdx(lib, strides=bad) == E
+    bad = list(ok); bad[6] = -1
+    assert _fwdx(lib, strides=bad) == E
+    bad = list(ok); bad[4], bad[5] = 8 * 4 * hd, 4 * hd                     # k and v token strides differ
+    assert _fwdx(lib, strides=bad) == U
+    bad = list(ok); bad[0], bad[1] = 8 * (3 * hd + 4), 3 * hd + 4           # bf16 q stride not 16-byte aligned
+    assert _fwdx(lib, strides=bad) == U
+    assert _fwdx(lib, q=ctypes.c_void_p(0x1008), strides=ok) == U         # misaligned bf16 q
+    bad = list(ok); bad[3] = bad[5] = 1 << 25                               # token stride too long
+    assert _fwdx(lib, strides=bad) == E
 
 
 def _bwd(lib, q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, ws=P, B=1, Sq=8, Sk=8, H=1, D=128, in_dt=1,
