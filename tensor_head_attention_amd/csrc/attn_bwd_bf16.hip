@@ -134,14 +134,6 @@ __device__ __forceinline__ void load_rows(bf16x8 (&f)[D / 16], const __bf16* bas
     f[t] = __builtin_bit_cast(bf16x8, buffer_load_16(rs, (uint32_t)lq * row_bytes + (uint32_t)(16 * t + 8 * hi) * 2));
 }
 
-// Pack accumulator elements 8h..8h+7 of block kb into the B operand of a 16-row step.
-__device__ __forceinline__ bf16x8 pack8(const f32x16& x, int h) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[8 * h + e];
-  return r;
-}
-
 // ---------------------------------------------------------------------------------------------
 // dq: 128 query rows per workgroup, 64-key tiles.
 template <int D>
@@ -222,6 +214,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(KArgs a) {
     if (!skip) {
       const char* kt_ = kbuf + buf * kTileBytes;
       const char* vt_ = vbuf + buf * kTileBytes;
+      // fenced phases, as in the dk/dv kernel
       f32x16 s[2], dp[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -232,25 +225,29 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(KArgs a) {
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(kt_, lq, hi, kb, t), qf[t], s[kb], 0, 0, 0);
           dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(vt_, lq, hi, kb, t), df[t], dp[kb], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // element j of block kb is key key0 + 32kb + 8(j/4) + 4hi + j%4 of this lane's query
+      // element j of block kb is key key0 + 32kb + 8(j/4) + 4hi + j%4 of this lane's query; it is
+      // hidden iff 32kb + 8(j/4) + j%4 >= bnd (one 32-bit compare and select per element)
       long long bound = lim_abs - key0;
       bound = bound < 0 ? 0 : (bound > kTile ? kTile : bound);
-      const int bnd = (int)bound - 4 * hi;
+      const int bnd = need_mask ? (int)bound - 4 * hi : kTile;
+      bf16x8 dsb[4];  // B operands of the 16-key steps ks = 2kb + j/8
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          float p = __builtin_amdgcn_exp2f(s[kb][j] * a.scale_log2 - Lc);
-          if (need_mask && kb * 32 + (j >> 2) * 8 + (j & 3) >= bnd) p = 0.f;
-          s[kb][j] = p * (dp[kb][j] - Dl);  // dS^T
+          const float e = __builtin_amdgcn_exp2f(s[kb][j] * a.scale_log2 - Lc);
+          const float p = kb * 32 + (j >> 2) * 8 + (j & 3) >= bnd ? 0.f : e;
+          dsb[2 * kb + (j >> 3)][j & 7] = (__bf16)(p * (dp[kb][j] - Dl));  // dS^T
         }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 dsb = pack8(s[ks >> 1], ks & 1);
 #pragma unroll
         for (int db = 0; db < kDBlocks; ++db)
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(kt_, lane, ks, db), dsb, acc[db], 0, 0, 0);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(kt_, lane, ks, db), dsb[ks], acc[db], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's share of tile kt+1 has landed in LDS
@@ -359,6 +356,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(KArgs a) {
     if (!skip) {
       const char* qt_ = qbuf + buf * kTileBytes;
       const char* dt_ = dbuf + buf * kTileBytes;
+      // The tile body runs in fenced phases (sched_barrier) so the scheduler does not hoist every
+      // LDS fragment of the tile at once, which would exceed the register file.
       f32x16 s[2], dp[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
@@ -369,12 +368,15 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(KArgs a) {
           s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qt_, lq, hi, qb, d), kf[d], s[qb], 0, 0, 0);
           dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(dt_, lq, hi, qb, d), vf[d], dp[qb], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // element j of block qb is query qt0_row + 32qb + 8(j/4) + 4hi + j%4 against this lane's key
-      long long thr = qmin - qt0_row - 4 * hi;  // hidden iff 32qb + 8(j/4) + j%4 < thr
+      // element j of block qb is query qt0_row + 32qb + 8(j/4) + 4hi + j%4 against this lane's key;
+      // it is hidden iff 32qb + 8(j/4) + j%4 < ithr (one 32-bit compare and select per element;
+      // a padding key hides all, a tile without causal overlap none)
+      long long thr = qmin - qt0_row - 4 * hi;
       thr = thr < -1 ? -1 : (thr > 2 * kTile ? 2 * kTile : thr);
-      const int ithr = (int)thr;
-      f32x16 p[2];
+      const int ithr = !key_live ? 2 * kTile : (need_mask ? (int)thr : -1);
+      bf16x8 pb[4], dsb[4];  // B operands of the 16-query steps ks = 2qb + j/8
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -384,21 +386,21 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(KArgs a) {
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const int j = 4 * g + jj;
-            float pv = __builtin_amdgcn_exp2f(s[qb][j] * a.scale_log2 - L4[jj]);
-            if (!key_live || (need_mask && qb * 32 + 8 * g + jj < ithr)) pv = 0.f;
-            p[qb][j] = pv;
-            s[qb][j] = pv * (dp[qb][j] - D4[jj]);  // dS
+            const float e = __builtin_amdgcn_exp2f(s[qb][j] * a.scale_log2 - L4[jj]);
+            const float pv = qb * 32 + 8 * g + jj < ithr ? 0.f : e;
+            pb[2 * qb + (j >> 3)][j & 7] = (__bf16)pv;
+            dsb[2 * qb + (j >> 3)][j & 7] = (__bf16)(pv * (dp[qb][j] - D4[jj]));  // dS
           }
         }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 pb = pack8(p[ks >> 1], ks & 1);
-        const bf16x8 dsb = pack8(s[ks >> 1], ks & 1);
 #pragma unroll
         for (int db = 0; db < kDBlocks; ++db) {
-          accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(dt_, lane, ks, db), pb, accv[db], 0, 0, 0);
-          acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qt_, lane, ks, db), dsb, acck[db], 0, 0, 0);
+          accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(dt_, lane, ks, db), pb[ks], accv[db], 0, 0, 0);
+          acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qt_, lane, ks, db), dsb[ks], acck[db], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
