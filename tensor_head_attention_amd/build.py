@@ -29,9 +29,17 @@ CFLAGS = [
 ]
 
 
+# Per-file code-generation options.  The backward kernels are compiler-scheduled with several
+# live accumulator sets; the VGPR form of MFMA keeps their results out of AGPRs, which otherwise
+# cost a copy back for every element the softmax-gradient step touches.
+FILE_FLAGS = {
+    "attn_bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(l for l in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
