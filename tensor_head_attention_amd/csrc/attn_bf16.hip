@@ -337,28 +337,40 @@ hipError_t launch_d(const AttnArgs& x, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Head size 128: the wide kernel (256 rows per workgroup, one workgroup per CU) when its grid
-// fills every CU at least twice, else the narrow one (128 rows, two workgroups per CU), which
-// keeps small grids spread over the chip.  THA_ATTN_D128_KERNEL=narrow|wide forces a choice.
-bool use_wide_d128(const AttnArgs& a) {
+// Head size 128, by grid size (CU count read once per device): the wide kernel (256 rows per
+// workgroup, one workgroup per CU) when its grid fills every CU at least twice; else the narrow
+// one (128 rows, two workgroups per CU) when its grid does; else the narrow kernel in split form
+// (two wavefront groups per workgroup share the key range), so small grids still put two
+// wavefronts on every SIMD.  THA_ATTN_D128_KERNEL=narrow|wide|split forces a choice.
+enum class D128 { kNarrow, kWide, kSplit };
+
+D128 choose_d128(const AttnArgs& a) {
   const char* force = getenv("THA_ATTN_D128_KERNEL");
-  if (force && strcmp(force, "wide") == 0) return true;
-  if (force && strcmp(force, "narrow") == 0) return false;
+  if (force && strcmp(force, "wide") == 0) return D128::kWide;
+  if (force && strcmp(force, "narrow") == 0) return D128::kNarrow;
+  if (force && strcmp(force, "split") == 0) return D128::kSplit;
   static int cu_count[64];  // per device, filled on first use
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return D128::kNarrow;
   if (cu_count[dev] == 0) {
     int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return false;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return D128::kNarrow;
     cu_count[dev] = n;
   }
-  return attn_bf16_d128_wide_blocks(a) >= 2 * (int64_t)cu_count[dev];
+  if (attn_bf16_d128_wide_blocks(a) >= 2 * (int64_t)cu_count[dev]) return D128::kWide;
+  if (attn_bf16_d128_blocks(a) >= 2 * (int64_t)cu_count[dev]) return D128::kNarrow;
+  return D128::kSplit;
 }
 
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
-  if (a.D == 128) return use_wide_d128(a) ? launch_attn_bf16_d128_wide(a, st) : launch_attn_bf16_d128(a, st);
+  if (a.D == 128) {
+    const D128 k = choose_d128(a);
+    if (k == D128::kWide) return launch_attn_bf16_d128_wide(a, st);
+    return launch_attn_bf16_d128(a, st, k == D128::kSplit);
+  }
   if (a.D == 64) return launch_d<64>(a, st);
   return hipErrorInvalidValue;
 }

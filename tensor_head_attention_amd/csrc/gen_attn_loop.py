@@ -10,6 +10,8 @@ Per 64-key tile t, for a wavefront of 32 query rows (the kernel source explains 
            tile t+1;
   then the lazy running-max update, the copies of later tiles into LDS, and the barrier.
 Fragments are read from LDS three MFMAs ahead; each wait covers exactly the fragment needed.
+The loop runs over nkt tiles starting at key tile tbase (0, or the second half of the key range
+when two wavefront groups of one workgroup split the keys); tmask counts from tbase.
 
 Register map (physical VGPRs, pinned by the operand constraints):
   O^T[db]   a[16db : 16db+15]           (fp32 accumulators in AGPRs, 4 blocks of 32 dims)
@@ -215,7 +217,8 @@ def dma(A, which, buf, lbl_skip, ahead):
     A.e(f"s_cmp_lt_u32 {sr(S_TMP)}, %[nkt]")
     A.e(f"s_cbranch_scc0 {lbl_skip}")
     # rows valid = min(64, kv_lim - 64*(t+ahead)); bytes = rows * row_bytes
-    A.e(f"s_lshl_b32 {sr(S_ROWS)}, {sr(S_TMP)}, 6")
+    A.e(f"s_add_u32 {sr(S_ROWS)}, {sr(S_TMP)}, %[tbase]")         # tile index in the key tensor
+    A.e(f"s_lshl_b32 {sr(S_ROWS)}, {sr(S_ROWS)}, 6")
     A.e(f"s_sub_i32 {sr(S_ROWS)}, %[kvlim], {sr(S_ROWS)}")
     A.e(f"s_min_i32 {sr(S_ROWS)}, {sr(S_ROWS)}, 64")
     A.e(f"s_mul_i32 {sr(rsrc + 2)}, {sr(S_ROWS)}, %[rowb]")
@@ -246,7 +249,8 @@ def half(A, parity, uid):
     A.e(f"s_add_u32 {sr(S_T1)}, {sr(S_T)}, 1")
     A.e(f"s_cmp_lt_u32 {sr(S_T1)}, %[nkt]")
     A.e(f"s_cbranch_scc0 Llast{p}")
-    A.e(f"s_lshl_b32 {sr(S_KEY)}, {sr(S_T1)}, 6")
+    A.e(f"s_add_u32 {sr(S_KEY)}, {sr(S_T1)}, %[tbase]")
+    A.e(f"s_lshl_b32 {sr(S_KEY)}, {sr(S_KEY)}, 6")
     A.e(f"s_cmp_ge_u32 {sr(S_T1)}, %[tmask]")
     A.e(f"s_cbranch_scc1 Lmask{p}")
     block(A, cur_base, nxt_base, kb_read, vb_read, True, False)

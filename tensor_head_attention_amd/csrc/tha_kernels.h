@@ -61,7 +61,8 @@ hipError_t launch_merge_lse(int n_parts, const PartPtrs& parts, int part_dt, voi
                             int B, int S, int H, int D, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
-hipError_t launch_attn_bf16_d128(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attn_bf16_d128(const AttnArgs& a, hipStream_t stream, bool split);
+int64_t attn_bf16_d128_blocks(const AttnArgs& a);
 hipError_t launch_attn_bf16_d128_wide(const AttnArgs& a, hipStream_t stream);
 int64_t attn_bf16_d128_wide_blocks(const AttnArgs& a);
 hipError_t launch_attn_bwd_delta(const AttnBwdArgs& a, int in_dt, hipStream_t stream);

@@ -56,7 +56,7 @@ def check_lse(dev_lse: torch.Tensor, ref: torch.Tensor, in_dtype: torch.dtype, w
 
 @contextlib.contextmanager
 def d128_kernel(name):
-    """Force the bf16 head-size-128 attention kernel (narrow / wide; None = automatic choice)
+    """Force the bf16 head-size-128 attention kernel (narrow / wide / split; None = automatic choice)
     for the calls inside, through the library's THA_ATTN_D128_KERNEL variable."""
     old = os.environ.get("THA_ATTN_D128_KERNEL")
     if name is None:

@@ -59,7 +59,7 @@ def _id(c):
 
 # every case on the automatic choice; the bf16 head-size-128 cases also on each kernel forced
 KCASES = [(c, None) for c in CASES] + [(c, kn) for c in CASES if c[4] == 128 and c[5] == torch.bfloat16
-                                       for kn in ("narrow", "wide")]
+                                       for kn in ("narrow", "wide", "split")]
 
 
 @pytest.mark.parametrize("case,kernel", KCASES, ids=lambda x: _id(x) if isinstance(x, tuple) else str(x))
