@@ -72,11 +72,12 @@ __device__ __forceinline__ int clamp_kv(const int* kv_len, int b, int Sk) {
   return L < 0 ? 0 : (L > Sk ? Sk : L);
 }
 
-// Per-lane offsets for copying a 64-row tile (rows of row_bytes, D bf16) into LDS, swizzled on
-// the global side so the LDS side is written linearly: wave w issues D/32 copies of 512/D rows.
-template <int D>
+// Per-lane offsets for copying a tile of R rows (rows of row_bytes, D bf16) into LDS, swizzled on
+// the global side so the LDS side is written linearly: wave w issues R*D/2048 copies of 512/D rows
+// (each copy is 64 lanes x 16 bytes = 1 KiB).
+template <int D, int R = 64>
 struct TileCopy {
-  static constexpr int kLoads = D / 32;       // per wave per tile
+  static constexpr int kLoads = R * D / 2048;  // per wave per tile
   static constexpr int kRowsPerLoad = 512 / D;
   static constexpr int kChunks = D / 8;
   uint32_t off[kLoads];
@@ -88,9 +89,9 @@ struct TileCopy {
       off[u] = (uint32_t)r * row_bytes + (uint32_t)((p ^ swz<D>(r)) * 16);
     }
   }
-  // rows [row0, row0 + 64) of a tensor whose row 0 is at base; rows >= valid_end read 0
+  // rows [row0, row0 + R) of a tensor whose row 0 is at base; rows >= valid_end read 0
   __device__ void copy(const __bf16* base, int64_t row_stride, int row0, int valid_end, char* dst, int wave) const {
-    const int rows_valid = min(kTile, valid_end - row0);
+    const int rows_valid = min(R, valid_end - row0);
     const i32x4 rs = make_rsrc_words(base + (int64_t)row0 * row_stride,
                                      (uint32_t)max(rows_valid, 0) * (uint32_t)(row_stride * 2));
     const uint32_t l = lds_addr(dst + wave * kLoads * 1024);
@@ -268,12 +269,18 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(KArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// dk, dv: 128 keys per workgroup, 64-query tiles.
+// dk, dv: 128 keys per workgroup, 32-query tiles.  K^T is register-resident (B operand of S);
+// the workgroup's 128 V rows sit in LDS for the whole kernel (B operand of dP, read as row
+// fragments), so a wavefront needs ~250 registers and two workgroups (2 x 64.5 KiB of LDS for
+// D = 128) share a CU: two wavefronts per SIMD.
+constexpr int kTq = 32;  // query rows per streamed tile of the dk/dv kernel
+
 template <int D>
-__global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(KArgs a) {
-  constexpr int kDSteps = D / 16, kDBlocks = D / 32, kTileBytes = kTile * D * 2;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];  // Q[0], Q[1], dO[0], dO[1]
-  __shared__ __attribute__((aligned(16))) float lt[2][kTile], dt[2][kTile];  // lse*log2(e) (+inf: P = 0), Delta
+__global__ void __launch_bounds__(kThreads, 2) bwd_dkdv_kernel(KArgs a) {
+  constexpr int kDSteps = D / 16, kDBlocks = D / 32, kTileBytes = kTq * D * 2;
+  // V rows of this workgroup, then Q[0], Q[1], dO[0], dO[1]
+  __shared__ __attribute__((aligned(1024))) char smem[kBlockRows * D * 2 + 4 * kTileBytes];
+  __shared__ __attribute__((aligned(16))) float lt[2][kTq], dt[2][kTq];  // lse*log2(e) (+inf: P = 0), Delta
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lq = lane & 31, hi = lane >> 5;
@@ -290,30 +297,36 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(KArgs a) {
     const long long f = a.k_pos0 + key_first - a.q_pos0;
     q_begin = f < 0 ? 0 : f;
   }
-  const int qt0 = (int)(q_begin / kTile);
-  const int n_qt = (a.Sq + kTile - 1) / kTile;
+  const int qt0 = (int)(q_begin / kTq);
+  const int n_qt = (a.Sq + kTq - 1) / kTq;
 
   const int k0 = key_first + wave * kRowsPerWave;
   const __bf16* kbase = a.k + (int64_t)b * a.Sk * rs + (int64_t)h * D;
   const __bf16* vbase = a.v + (int64_t)b * a.Sk * rs + (int64_t)h * D;
-  bf16x8 kf[kDSteps], vf[kDSteps];
+  bf16x8 kf[kDSteps];
   load_rows<D>(kf, kbase, rs, k0, kv_lim, lq, hi);
-  load_rows<D>(vf, vbase, rs, k0, kv_lim, lq, hi);
   const int key = k0 + lq;
   const bool key_live = key < kv_lim;
   // causal: query index i sees this lane's key iff i >= qmin
   long long qmin = 0;
   if (a.causal) qmin = a.k_pos0 + key - a.q_pos0;
 
-  TileCopy<D> cp;
+  char* const vrows = smem;
+  char* const qbuf = smem + kBlockRows * D * 2;
+  char* const dbuf = qbuf + 2 * kTileBytes;
+  {
+    TileCopy<D, 64> vc;  // the 128 V rows as two 64-row halves (the swizzle depends on row % 16 only)
+    vc.init(wave, lane, (uint32_t)(rs * 2));
+    vc.copy(vbase, rs, key_first, kv_lim, vrows, wave);
+    vc.copy(vbase, rs, key_first + 64, kv_lim, vrows + 64 * D * 2, wave);
+  }
+  TileCopy<D, kTq> cp;
   cp.init(wave, lane, (uint32_t)(rs * 2));
   const __bf16* qbase = a.q + (int64_t)b * a.Sq * rs + (int64_t)h * D;
   const __bf16* dbase = a.dout + (int64_t)b * a.Sq * rs + (int64_t)h * D;
-  char* const qbuf = smem;
-  char* const dbuf = smem + 2 * kTileBytes;
-  auto stats = [&](int t, int slot) {  // lse and Delta of the 64 rows of query tile t
-    if (tid < kTile) {
-      const int r = t * kTile + tid;
+  auto stats = [&](int t, int slot) {  // lse and Delta of the 32 rows of query tile t
+    if (tid < kTq) {
+      const int r = t * kTq + tid;
       float L = INFINITY, Dv = 0.f;
       if (r < a.Sq) {
         const float l = a.lse[(int64_t)bh * a.Sq + r];
@@ -332,8 +345,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(KArgs a) {
     for (int j = 0; j < 16; ++j) acck[i][j] = accv[i][j] = 0.f;
 
   if (qt0 < n_qt) {
-    cp.copy(qbase, rs, qt0 * kTile, a.Sq, qbuf, wave);
-    cp.copy(dbase, rs, qt0 * kTile, a.Sq, dbuf, wave);
+    cp.copy(qbase, rs, qt0 * kTq, a.Sq, qbuf, wave);
+    cp.copy(dbase, rs, qt0 * kTq, a.Sq, dbuf, wave);
     stats(qt0, 0);
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -341,66 +354,62 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(KArgs a) {
   for (int t = qt0; t < n_qt; ++t) {
     const int buf = (t - qt0) & 1;
     if (t + 1 < n_qt) {
-      cp.copy(qbase, rs, (t + 1) * kTile, a.Sq, qbuf + (buf ^ 1) * kTileBytes, wave);
-      cp.copy(dbase, rs, (t + 1) * kTile, a.Sq, dbuf + (buf ^ 1) * kTileBytes, wave);
+      cp.copy(qbase, rs, (t + 1) * kTq, a.Sq, qbuf + (buf ^ 1) * kTileBytes, wave);
+      cp.copy(dbase, rs, (t + 1) * kTq, a.Sq, dbuf + (buf ^ 1) * kTileBytes, wave);
       stats(t + 1, buf ^ 1);
     }
-    const int qt0_row = t * kTile;
+    const int qt0_row = t * kTq;
     bool skip = k0 >= kv_lim;
     bool need_mask = false;
     if (a.causal) {
       // wave keys k0 .. k0+31 are seen by queries >= k_pos0 + key - q_pos0
-      if ((long long)qt0_row + kTile - 1 < a.k_pos0 + k0 - a.q_pos0) skip = true;
+      if ((long long)qt0_row + kTq - 1 < a.k_pos0 + k0 - a.q_pos0) skip = true;
       if ((long long)qt0_row < a.k_pos0 + k0 + kRowsPerWave - 1 - a.q_pos0) need_mask = true;
     }
     if (!skip) {
       const char* qt_ = qbuf + buf * kTileBytes;
       const char* dt_ = dbuf + buf * kTileBytes;
       // The tile body runs in fenced phases (sched_barrier) so the scheduler does not hoist every
-      // LDS fragment of the tile at once, which would exceed the register file.
-      f32x16 s[2], dp[2];
+      // LDS fragment of the tile at once, which would exceed the register budget.
+      f32x16 s, dp;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int j = 0; j < 16; ++j) s[j] = dp[j] = 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) s[qb][j] = dp[qb][j] = 0.f;
-#pragma unroll
-        for (int d = 0; d < kDSteps; ++d) {
-          s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qt_, lq, hi, qb, d), kf[d], s[qb], 0, 0, 0);
-          dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(dt_, lq, hi, qb, d), vf[d], dp[qb], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int d = 0; d < kDSteps; ++d) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(qt_, lq, hi, 0, d), kf[d], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(dt_, lq, hi, 0, d), row_frag<D>(vrows, lq, hi, wave, d),
+                                                     dp, 0, 0, 0);
+        if (d % 4 == 3) __builtin_amdgcn_sched_barrier(0);
       }
-      // element j of block qb is query qt0_row + 32qb + 8(j/4) + 4hi + j%4 against this lane's key;
-      // it is hidden iff 32qb + 8(j/4) + j%4 < ithr (one 32-bit compare and select per element;
-      // a padding key hides all, a tile without causal overlap none)
+      // element j is query qt0_row + 8(j/4) + 4hi + j%4 against this lane's key; it is hidden iff
+      // 8(j/4) + j%4 < ithr (one 32-bit compare and select per element; a padding key hides all,
+      // a tile without causal overlap none)
       long long thr = qmin - qt0_row - 4 * hi;
-      thr = thr < -1 ? -1 : (thr > 2 * kTile ? 2 * kTile : thr);
-      const int ithr = !key_live ? 2 * kTile : (need_mask ? (int)thr : -1);
-      bf16x8 pb[4], dsb[4];  // B operands of the 16-query steps ks = 2qb + j/8
+      thr = thr < -1 ? -1 : (thr > 2 * kTq ? 2 * kTq : thr);
+      const int ithr = !key_live ? 2 * kTq : (need_mask ? (int)thr : -1);
+      bf16x8 pb[2], dsb[2];  // B operands of the 16-query steps ks = j/8
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 L4 = *(const f32x4*)&lt[buf][8 * g + 4 * hi];
+        const f32x4 D4 = *(const f32x4*)&dt[buf][8 * g + 4 * hi];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 L4 = *(const f32x4*)&lt[buf][qb * 32 + 8 * g + 4 * hi];
-          const f32x4 D4 = *(const f32x4*)&dt[buf][qb * 32 + 8 * g + 4 * hi];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const int j = 4 * g + jj;
-            const float e = __builtin_amdgcn_exp2f(s[qb][j] * a.scale_log2 - L4[jj]);
-            const float pv = qb * 32 + 8 * g + jj < ithr ? 0.f : e;
-            pb[2 * qb + (j >> 3)][j & 7] = (__bf16)pv;
-            dsb[2 * qb + (j >> 3)][j & 7] = (__bf16)(pv * (dp[qb][j] - D4[jj]));  // dS
-          }
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = 4 * g + jj;
+          const float e = __builtin_amdgcn_exp2f(s[j] * a.scale_log2 - L4[jj]);
+          const float pv = 8 * g + jj < ithr ? 0.f : e;
+          pb[j >> 3][j & 7] = (__bf16)pv;
+          dsb[j >> 3][j & 7] = (__bf16)(pv * (dp[j] - D4[jj]));  // dS
         }
+      }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
         for (int db = 0; db < kDBlocks; ++db) {
           accv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(dt_, lane, ks, db), pb[ks], accv[db], 0, 0, 0);
           acck[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(qt_, lane, ks, db), dsb[ks], acck[db], 0, 0, 0);
+          if (db % 2 == 1) __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
