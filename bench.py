@@ -157,10 +157,14 @@ def main():
                      "frac_mfma_peak": attn_tflops / PEAK_BF16_TFLOPS},
     }
 
-    # shard_permute alone, timed in batches of back-to-back calls (Q, K, V shards in turn, as in
-    # the step; 3 x 64 MiB of distinct reads per round, so the reads come from HBM)
+    # shard_permute alone, timed in batches of back-to-back calls: Q, K, V shards in turn, each
+    # round on the next head group, so consecutive calls read distinct 64 MiB slices (24 x 64 MiB
+    # before one repeats, far more than the 256 MiB MALL): the reads come from HBM
+    # (into a buffer of their own: the step's grouped tensors feed the backward side figure)
     names = ("q", "k", "v")
-    pb = batch_times(torch, lambda i: T.shard_permute(shards[names[i % 3]], grp, out=grouped[names[i % 3]]))
+    pout = torch.empty_like(grouped["q"])
+    pb = batch_times(torch, lambda i: T.shard_permute(shards[names[i % 3]], (i // 3) % P, out=pout))
+    del pout
     components["shard_permute_batched"] = {"us_per_call": pb[len(pb) // 2] * 1e3, "us_min": pb[0] * 1e3,
                                            "timing": BATCH_NOTE,
                                            "GB_per_s": permute_bytes / (pb[len(pb) // 2] * 1e-3) / 1e9,
@@ -183,6 +187,7 @@ def main():
         components.update(bwd_side(T, W, torch, dev, grouped, out, lse, S, Hl, D, flops, args.seed))
         components.update(ring_side(T, W, torch, dev, args.seed))
         components.update(merge_rotating(T, torch, dev))
+        components.update(config_side(T, W, torch, dev))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -333,6 +338,39 @@ def ring_side(T, W, torch, dev, seed):
                                 "GB_per_s": merge_bytes / (merge_ms * 1e-3) / 1e9,
                                 "frac_hbm_peak": merge_bytes / (merge_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
     }
+
+
+def config_side(T, W, torch, dev):
+    """attn_fwd at the two other bf16 workloads: causal S=4096 x 8 heads (one 128-row query tile per
+    workgroup and head: 256 workgroups, the split kernel form), and the padded batch B=4, S=8192,
+    32 heads, non-causal, key lengths drawn per sequence (the wide kernel)."""
+    res = {}
+    inp, p = W.workload_inputs(2)
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    S, H, D = p["S"], p["H"], p["D"]
+    o = torch.empty_like(q)
+    l = torch.empty((1, H, S), dtype=torch.float32, device=dev)
+    t = batch_times(torch, lambda i: T.attn_fwd(q, k, v, causal=True, out=o, lse=l), batches=5, n=20)
+    ms = t[len(t) // 2]
+    flops = 4.0 * D * H * causal_pairs(S, S, 0, 0)
+    res["workload2_causal_4k"] = {"us": ms * 1e3, "flop": flops, "TFLOP_per_s": flops / (ms * 1e-3) / 1e12,
+                                  "frac_mfma_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                  "timing": "median over 5 batches of 20 back-to-back calls, one event pair per batch"}
+    del q, k, v, o, l, inp
+    inp, p = W.workload_inputs(5)
+    B, S, H, D = p["B"], p["S"], p["H"], p["D"]
+    q, k, v, kv = (inp[n].to(dev) for n in ("q", "k", "v", "kv_len"))
+    lens = inp["kv_len"].tolist()
+    o = torch.empty_like(q)
+    l = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    t = batch_times(torch, lambda i: T.attn_fwd(q, k, v, kv_len=kv, out=o, lse=l), batches=3, n=5)
+    ms = t[len(t) // 2]
+    flops = 4.0 * D * H * S * float(sum(lens))
+    res["workload5_padded_batch"] = {"ms": ms, "flop": flops, "kv_len": lens,
+                                     "TFLOP_per_s": flops / (ms * 1e-3) / 1e12,
+                                     "frac_mfma_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                     "timing": "median over 3 batches of 5 back-to-back calls, one event pair per batch"}
+    return res
 
 
 def merge_rotating(T, torch, dev, n=8, S=4096, H=8, D=128, sets=3):

@@ -36,9 +36,10 @@
 //  * Masking (causal with global positions, key padding, sequence tails) is
 //    applied only on tiles that need it; tiles wholly in a wavefront's future
 //    are skipped.  Out-of-range loads return zero (buffer range checking).
-//  * Heaviest causal query tiles are launched first; consecutive workgroups
-//    take different heads of one query tile, so each head's workgroups land on
-//    one XCD (dispatch is round-robin over the 8 XCDs) and share its L2.
+//  * Heaviest causal query tiles are launched first, and the workgroups that
+//    one XCD receives (dispatch is round-robin over the 8 XCDs) walk one
+//    (batch, head) at a time, so they share that head's K/V in the XCD's L2
+//    (work_item in device_common.h).
 #include <cstdlib>
 #include <cstring>
 
@@ -108,8 +109,8 @@ __global__ void __launch_bounds__(kThreads, 2) attn_bf16_kernel(KernelArgs a) {
   const int hi = lane >> 5;   // half-wave
   const int BH = a.B * a.H;
   const int n_qt = (a.Sq + kBlockM - 1) / kBlockM;
-  const int qt = n_qt - 1 - (int)(blockIdx.x / BH);  // heaviest causal tiles first
-  const int bh = (int)(blockIdx.x % BH);
+  const WorkItem wi = work_item((int)blockIdx.x, n_qt, BH, true);  // heaviest causal tiles first
+  const int qt = wi.tile, bh = wi.bh;
   const int b = bh / a.H, h = bh % a.H;
   const int64_t row_stride = a.k_rs;                // K/V elements between consecutive tokens
   const uint32_t row_bytes = (uint32_t)(row_stride * 2);

@@ -27,7 +27,8 @@
 // x 4 chunks per half-wave) use one XOR swizzle of the chunk index that is a bijection for both
 // patterns: D = 128: chunk ^ ((row & 3) << 2 | (row >> 2) & 3); D = 64 (two rows per bank line):
 // chunk ^ (((row >> 1) & 1) << 2 | (row >> 2) & 3).  Tiles are copied by buffer_load ... lds,
-// double buffered.  Both kernels launch heaviest causal blocks first.
+// double buffered.  Both kernels launch heaviest causal blocks first, in the XCD-aware order of
+// work_item (device_common.h).
 #include "device_common.h"
 #include "tha_kernels.h"
 
@@ -146,8 +147,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(KArgs a) {
   const int lane = tid & 63, lq = lane & 31, hi = lane >> 5;
   const int BH = a.B * a.H;
   const int n_qt = (a.Sq + kBlockRows - 1) / kBlockRows;
-  const int qt = n_qt - 1 - (int)(blockIdx.x / BH);
-  const int bh = (int)(blockIdx.x % BH);
+  const WorkItem wi = work_item((int)blockIdx.x, n_qt, BH, true);
+  const int qt = wi.tile, bh = wi.bh;
   const int b = bh / a.H, h = bh % a.H;
   const int64_t rs = (int64_t)a.H * D;
   const int kv_lim = clamp_kv(a.kv_len, b, a.Sk);
@@ -285,8 +286,9 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dkdv_kernel(KArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, lq = lane & 31, hi = lane >> 5;
   const int BH = a.B * a.H;
-  const int kblk = (int)(blockIdx.x / BH);  // ascending: the earliest keys are seen by the most queries
-  const int bh = (int)(blockIdx.x % BH);
+  // ascending: the earliest keys are seen by the most queries
+  const WorkItem wi = work_item((int)blockIdx.x, (a.Sk + kBlockRows - 1) / kBlockRows, BH, false);
+  const int kblk = wi.tile, bh = wi.bh;
   const int b = bh / a.H, h = bh % a.H;
   const int64_t rs = (int64_t)a.H * D;
   const int kv_lim = clamp_kv(a.kv_len, b, a.Sk);

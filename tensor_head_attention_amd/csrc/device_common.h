@@ -95,6 +95,31 @@ __device__ __forceinline__ MergeW merge_weights(float lse_r, float lse_c) {
   return {wr / W, wc / W, M + logf(W)};
 }
 
+// Work order of the attention kernels: workgroup `blk` of a grid of n_tiles x BH (tile index,
+// (batch, head)) items.  Workgroups reach the 8 XCDs round-robin (blk % 8), each XCD with its own
+// L2.  When BH is a multiple of 8, the workgroups one XCD receives walk one (batch, head) at a time,
+// so the K/V (or Q/dO) rows they stream are shared in that XCD's L2; otherwise consecutive
+// workgroups take consecutive (batch, head)s.  Within a (batch, head) the tiles come in the order
+// `first`, first +- 1, ... (`descending` = last tile first).  Any order is correct: it is a bijection
+// of [0, n_tiles * BH).
+constexpr int kXcds = 8;
+struct WorkItem {
+  int tile, bh;
+};
+__device__ __forceinline__ WorkItem work_item(int blk, int n_tiles, int BH, bool descending) {
+  int t, bh;
+  if (BH % kXcds == 0) {
+    const int x = blk % kXcds, slot = blk / kXcds;
+    const int bl = slot / n_tiles;
+    t = slot - bl * n_tiles;
+    bh = bl * kXcds + x;
+  } else {
+    t = blk / BH;
+    bh = blk - t * BH;
+  }
+  return {descending ? n_tiles - 1 - t : t, bh};
+}
+
 // Round-to-nearest-even fp32 -> bf16 pair (the hardware conversion on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16x2 v = {(__bf16)a, (__bf16)b};
