@@ -35,9 +35,10 @@ def check_out(dev_out: torch.Tensor, ref: torch.Tensor, in_dtype: torch.dtype, w
     tol = TOL[in_dtype]
     diff = (o - ref).abs()
     max_abs = diff.max().item() if diff.numel() else 0.0
+    rel = ((o - ref).norm() / ref.norm().clamp_min(1e-300)).item() if ref.numel() else 0.0
+    say(f"  {what}: max-abs {max_abs:.3e}, rel-L2 {rel:.3e}")
     assert max_abs <= tol["max_abs"], f"{what}: max-abs {max_abs:.3e} > {tol['max_abs']}"
     if tol["rel_l2"] is not None and ref.numel():
-        rel = ((o - ref).norm() / ref.norm().clamp_min(1e-300)).item()
         assert rel <= tol["rel_l2"], f"{what}: rel-L2 {rel:.3e} > {tol['rel_l2']}"
     return max_abs
 
@@ -51,6 +52,7 @@ def check_lse(dev_lse: torch.Tensor, ref: torch.Tensor, in_dtype: torch.dtype, w
     fin = ~inf_ref
     if fin.any():
         err = (l[fin] - ref[fin]).abs().max().item()
+        say(f"  {what}: max-abs {err:.3e}")
         assert err <= TOL[in_dtype]["lse"], f"{what}: max-abs {err:.3e} > {TOL[in_dtype]['lse']}"
 
 
