@@ -278,3 +278,32 @@ def shard_unpermute(x: torch.Tensor, group: int, shards: Sequence[torch.Tensor])
     rc = _lib.shard_unpermute(x.data_ptr(), P, int(group), _ptrs(shards), B, S, Hl * P, D, x.element_size(),
                               _stream(x))
     _check(rc, "shard_unpermute")
+
+
+class _Attention(torch.autograd.Function):
+    """Differentiable attention: attn_fwd forward, attn_bwd backward (saved o and lse)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal, kv_len, q_pos0, k_pos0, scale):
+        o, lse = attn_fwd(q, k, v, causal=causal, kv_len=kv_len, q_pos0=q_pos0, k_pos0=k_pos0, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.kv_len = kv_len
+        ctx.opts = (causal, q_pos0, k_pos0, scale)
+        return o
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, o, lse = ctx.saved_tensors
+        causal, q_pos0, k_pos0, scale = ctx.opts
+        dq, dk, dv = attn_bwd(q, k, v, o, dout.to(q.dtype).contiguous(), lse, causal=causal, kv_len=ctx.kv_len,
+                              q_pos0=q_pos0, k_pos0=k_pos0, scale=scale)
+        # the gradients are fp32 accumulators; autograd receives them in the inputs' dtype
+        return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None, None, None
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool = False,
+              kv_len: Optional[torch.Tensor] = None, q_pos0: int = 0, k_pos0: int = 0,
+              scale: Optional[float] = None) -> torch.Tensor:
+    """Attention output [B,Sq,H,D] (dtype of q) with autograd support: the forward runs attn_fwd,
+    the backward attn_bwd, both in the library's kernels."""
+    return _Attention.apply(q, k, v, causal, kv_len, q_pos0, k_pos0, scale)
