@@ -216,12 +216,19 @@ def main():
                      "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": attn_traffic(),
                      "avg_kernel_ms": round(attn_ms, 4)},
         "cpu_baseline": cpu,
+        "device": device_info(torch, dev),
         "components": components,
     }
     print(json.dumps(line), flush=True)
 
 
 BATCH_NOTE = "median over 5 batches of 30 back-to-back calls, one event pair per batch"
+
+
+def device_info(torch, dev):
+    pr = torch.cuda.get_device_properties(dev)
+    return {"name": pr.name, "arch": getattr(pr, "gcnArchName", ""), "compute_units": pr.multi_processor_count,
+            "memory_GiB": round(pr.total_memory / 2**30, 1)}
 
 
 def batch_times(torch, call, batches=5, n=30):
