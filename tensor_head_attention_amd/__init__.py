@@ -307,3 +307,36 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool
     """Attention output [B,Sq,H,D] (dtype of q) with autograd support: the forward runs attn_fwd,
     the backward attn_bwd, both in the library's kernels."""
     return _Attention.apply(q, k, v, causal, kv_len, q_pos0, k_pos0, scale)
+
+
+def ulysses_share(q_shards: Sequence[torch.Tensor], k_shards: Sequence[torch.Tensor],
+                  v_shards: Sequence[torch.Tensor], group: int, *, causal: bool = True,
+                  kv_len: Optional[torch.Tensor] = None, scale: Optional[float] = None):
+    """One GPU's Ulysses share: the P sequence shards [B,S/P,H,D] of Q, K and V are permuted to head
+    group `group` over the whole sequence (shard_permute) and attended (attn_fwd).
+    Returns (out [B,S,H/P,D], lse [B,H/P,S])."""
+    q, k, v = (shard_permute(s, group) for s in (q_shards, k_shards, v_shards))
+    return attn_fwd(q, k, v, causal=causal, kv_len=kv_len, scale=scale)
+
+
+def ring_share(q: torch.Tensor, k_chunks: Sequence[torch.Tensor], v_chunks: Sequence[torch.Tensor], *,
+               q_pos0: int, k_pos0s: Sequence[int], causal: bool = True, scale: Optional[float] = None,
+               fused: bool = True, out_dtype: Optional[torch.dtype] = None):
+    """One GPU's Ring share: the local Q chunk (first query at global position q_pos0) against K/V
+    chunks that arrive in turn (first key of chunk t at k_pos0s[t]).  fused=True merges each chunk's
+    result into a running fp32 (o, lse) in the attention epilogue (attn_fwd_ex with accumulate);
+    fused=False keeps fp32 partials and merges them once (attn_merge_lse).
+    Returns (out [B,Sq,H,D] in out_dtype (default q's), lse [B,H,Sq])."""
+    if len(k_chunks) != len(v_chunks) or len(k_chunks) != len(k_pos0s) or not k_chunks:
+        raise ValueError("need matching, non-empty k_chunks, v_chunks and k_pos0s")
+    B, Sq, H, D = q.shape
+    if fused:
+        o = torch.empty((B, Sq, H, D), dtype=torch.float32, device=q.device)
+        lse = torch.full((B, H, Sq), float("-inf"), dtype=torch.float32, device=q.device)
+        for kc, vc, kp in zip(k_chunks, v_chunks, k_pos0s):
+            attn_fwd_ex(q, kc, vc, causal=causal, q_pos0=q_pos0, k_pos0=kp, scale=scale, out=o, lse=lse,
+                        accumulate=True)
+        return attn_merge_lse([o], [lse], out_dtype=out_dtype or q.dtype)
+    parts = [attn_fwd(q, kc, vc, causal=causal, q_pos0=q_pos0, k_pos0=kp, scale=scale, out_dtype=torch.float32)
+             for kc, vc, kp in zip(k_chunks, v_chunks, k_pos0s)]
+    return attn_merge_lse([p[0] for p in parts], [p[1] for p in parts], out_dtype=out_dtype or q.dtype)
