@@ -40,6 +40,7 @@
 //    one XCD receives (dispatch is round-robin over the 8 XCDs) walk one
 //    (batch, head) at a time, so they share that head's K/V in the XCD's L2
 //    (work_item in device_common.h).
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
 
@@ -350,17 +351,17 @@ D128 choose_d128(const AttnArgs& a) {
   if (force && strcmp(force, "wide") == 0) return D128::kWide;
   if (force && strcmp(force, "narrow") == 0) return D128::kNarrow;
   if (force && strcmp(force, "split") == 0) return D128::kSplit;
-  static int cu_count[64];  // per device, filled on first use
+  static std::atomic<int> cu_count[64];  // per device, filled on first use (any thread may fill it)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return D128::kNarrow;
-  if (cu_count[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+  int cus = cu_count[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
       return D128::kNarrow;
-    cu_count[dev] = n;
+    cu_count[dev].store(cus, std::memory_order_relaxed);
   }
-  if (attn_bf16_d128_wide_blocks(a) >= 2 * (int64_t)cu_count[dev]) return D128::kWide;
-  if (attn_bf16_d128_blocks(a) >= 2 * (int64_t)cu_count[dev]) return D128::kNarrow;
+  if (attn_bf16_d128_wide_blocks(a) >= 2 * (int64_t)cus) return D128::kWide;
+  if (attn_bf16_d128_blocks(a) >= 2 * (int64_t)cus) return D128::kNarrow;
   return D128::kSplit;
 }
 
