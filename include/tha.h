@@ -93,10 +93,14 @@ enum {
  * section 3.2 casts the fp32 softmax back to the input type);
  * in_dt = THA_F32 with 1 <= D <= 256 (fp32 throughout).  out_dt may be THA_BF16
  * or THA_F32 in both cases (fp32 output keeps ring partials unrounded).
- * Kernel choice for bf16, D = 128: a wide kernel (256 query rows per workgroup)
- * when its grid holds at least two workgroups per compute unit, else a narrow one
- * (128 rows); both compute the same function.  The environment variable
- * THA_ATTN_D128_KERNEL=narrow|wide, read on every call, forces one of them.
+ * Kernel choice for bf16, D = 128, by grid size: a wide kernel (256 query rows per
+ * workgroup) when its grid holds at least two workgroups per compute unit, else a
+ * narrow one (128 rows) when its grid does, else the narrow kernel in split form
+ * (two wavefront groups per workgroup on the two halves of the key range, merged by
+ * log-sum-exp before the output is written).  All three compute the same function;
+ * the wide and narrow kernels give identical bits, the split form differs from them
+ * only by the association of the two key halves.  The environment variable
+ * THA_ATTN_D128_KERNEL=narrow|wide|split, read on every call, forces one of them.
  * Errors: THA_ERR_INVALID for null q/k/v/o, non-positive sizes, unknown mask
  * bits, KEY_PADDING without kv_len, scale not finite and positive, |q_pos0| or |k_pos0| >=
  * 2^62; THA_ERR_UNSUPPORTED for other dtypes / head dims.
