@@ -99,8 +99,10 @@ def issue_v(A, j):
     return A.lds(f"ds_read_b64_tr_b16 {vr(base + 2, 2)}, %[va{db}] offset:{ks * 4096 + 2048}")
 
 
-def block(A, cur, nxt, has_next, masked):
-    """One tile.  With has_next, K fragments 0..2 of tile t+1 are in flight at entry."""
+def block(A, cur, nxt, has_next, masked, extra_a=(), extra_b=()):
+    """One tile.  With has_next, K fragments 0..2 of tile t+1 are in flight at entry.
+    extra_a / extra_b: groups of scalar-unit work (tile copies, buffer rotation) issued after the
+    MFMA of slot i of phase A / B, so they run in the shadow of the matrix core."""
     A.n_ops = 0
     k_ops, v_ops = {}, {}
     if has_next:
@@ -155,6 +157,8 @@ def block(A, cur, nxt, has_next, masked):
                 f"{ar(A_Q + 32 * qb + 4 * tt, 4)}, {src2}")
             for op in slots_a[s]:
                 A.e(op)
+            for op in (extra_a[s] if s < len(extra_a) else []):
+                A.e(op)
     else:
         for jv in range(3):
             v_ops[jv] = issue_v(A, jv)
@@ -201,6 +205,8 @@ def block(A, cur, nxt, has_next, masked):
             A.e(cvt(31))  # last pair of P (read by the MFMAs of step ks = 3)
         for op in slots_b[s]:
             A.e(op)
+        for op in (extra_b[s] if s < len(extra_b) else []):
+            A.e(op)
 
     if has_next:
         A.e("s_nop 1")
@@ -214,10 +220,6 @@ def block(A, cur, nxt, has_next, masked):
             A.e(f"v_max_f32_e32 {vr(V_MX[qb])}, {vr(V_AL[qb])}, {vr(V_MX[qb])}")
     for qb in range(2):
         A.e(f"v_add_f32_e32 %[lrun{qb}], %[lrun{qb}], {vr(V_RS[qb])}")
-    # O^T (MFMA results) may be read by VALU next: keep >= 24 wait states
-    A.e("s_nop 7")
-    A.e("s_nop 7")
-    A.e("s_nop 7")
 
 
 def rescale(A, qb, lbl):
@@ -227,6 +229,10 @@ def rescale(A, qb, lbl):
     A.e(f"v_cmp_gt_f32_e32 vcc, {vr(mx)}, {vr(t0)}")
     A.e("s_nop 4")                                                        # VALU vcc -> vccz branch
     A.e(f"s_cbranch_vccz {lbl}")
+    # O^T, written by the value product just before, is read by VALU below: >= 24 wait states
+    A.e("s_nop 7")
+    A.e("s_nop 7")
+    A.e("s_nop 7")
     A.e(f"v_cndmask_b32_e32 {vr(t0)}, %[mrun{qb}], {vr(mx)}, vcc")     # m_new
     A.e(f"v_sub_f32_e32 {vr(al)}, %[mrun{qb}], {vr(t0)}")
     A.e(f"v_mul_f32_e32 {vr(al)}, %[c], {vr(al)}")
@@ -250,6 +256,15 @@ def rescale(A, qb, lbl):
     A.e(f"v_cndmask_b32_e64 %[nmc{qb}], %[nmc{qb}], 0, vcc")
 
 
+class Lines:
+    """Collects instruction lines (to be placed into MFMA slots later)."""
+    def __init__(self):
+        self.lines = []
+
+    def e(self, s):
+        self.lines.append(s)
+
+
 def buf_index(A, dst, add):
     """dst = (S_B0 + add) mod 3."""
     if add == 0:
@@ -261,31 +276,37 @@ def buf_index(A, dst, add):
     A.e(f"s_cselect_b32 {sr(dst)}, {sr(S_Y)}, {sr(dst)}")
 
 
-def dma(A, which, lbl_skip, ahead, buf_add):
-    """Copy tile t + ahead of K or V into LDS buffer (t + buf_add) mod 3 if it exists."""
+def dma_groups(which, ahead, buf_add):
+    """Copy of tile t + ahead of K or V into LDS buffer (t + buf_add) mod 3, without branches:
+    past the last tile the copy has 0 valid rows (no memory is read; the buffer it fills is not
+    read again).  Returned as groups of instructions, each group placed after one MFMA; every
+    SCC producer sits next to its consumer inside a group."""
     ptr, rsrc, offs, dst = (S_KP, S_KR, "koff", "kdst") if which == "k" else (S_VP, S_VR, "voff", "vdst")
-    A.e(f"s_add_u32 {sr(S_TMP)}, {sr(S_T)}, {ahead}")
-    A.e(f"s_cmp_lt_u32 {sr(S_TMP)}, %[nkt]")
-    A.e(f"s_cbranch_scc0 {lbl_skip}")
-    A.e(f"s_lshl_b32 {sr(S_ROWS)}, {sr(S_TMP)}, 6")           # rows = min(64, kv_lim - 64 (t + ahead))
-    A.e(f"s_sub_i32 {sr(S_ROWS)}, %[kvlim], {sr(S_ROWS)}")
-    A.e(f"s_min_i32 {sr(S_ROWS)}, {sr(S_ROWS)}, 64")
-    A.e(f"s_mul_i32 {sr(rsrc + 2)}, {sr(S_ROWS)}, %[rowb]")
-    A.e(f"s_mov_b32 {sr(rsrc)}, {sr(ptr)}")
-    A.e(f"s_and_b32 {sr(rsrc + 1)}, {sr(ptr + 1)}, 0xffff")
-    A.e(f"s_mov_b32 {sr(rsrc + 3)}, 0x20000")
-    buf_index(A, S_X, buf_add)
-    A.e(f"s_lshl_b32 {sr(S_X)}, {sr(S_X)}, 14")
-    A.e(f"s_add_u32 {sr(S_TMP)}, %[{dst}0], {sr(S_X)}")
+    g = []
+    g.append([f"s_add_u32 {sr(S_TMP)}, {sr(S_T)}, {ahead}",
+              f"s_lshl_b32 {sr(S_ROWS)}, {sr(S_TMP)}, 6",          # rows = min(64, kv_lim - 64 (t + ahead))
+              f"s_sub_i32 {sr(S_ROWS)}, %[kvlim], {sr(S_ROWS)}",
+              f"s_min_i32 {sr(S_ROWS)}, {sr(S_ROWS)}, 64",
+              f"s_max_i32 {sr(S_ROWS)}, {sr(S_ROWS)}, 0",
+              f"s_cmp_lt_u32 {sr(S_TMP)}, %[nkt]",                  # no such tile: 0 rows
+              f"s_cselect_b32 {sr(S_ROWS)}, {sr(S_ROWS)}, 0"])
+    g.append([f"s_mul_i32 {sr(rsrc + 2)}, {sr(S_ROWS)}, %[rowb]",
+              f"s_mov_b32 {sr(rsrc)}, {sr(ptr)}",
+              f"s_and_b32 {sr(rsrc + 1)}, {sr(ptr + 1)}, 0xffff",
+              f"s_mov_b32 {sr(rsrc + 3)}, 0x20000"])
+    b = Lines()
+    buf_index(b, S_X, buf_add)
+    b.e(f"s_lshl_b32 {sr(S_X)}, {sr(S_X)}, 14")
+    b.e(f"s_add_u32 {sr(S_TMP)}, %[{dst}0], {sr(S_X)}")
+    g.append(b.lines)
     for u in range(4):
-        A.e(f"s_mov_b32 m0, {sr(S_TMP)}")
-        A.e("s_nop 0")
-        A.e(f"buffer_load_dwordx4 %[{offs}{u}], {sr(rsrc, 4)}, 0 offen lds")
+        c = [f"s_mov_b32 m0, {sr(S_TMP)}", "s_nop 0", f"buffer_load_dwordx4 %[{offs}{u}], {sr(rsrc, 4)}, 0 offen lds"]
         if u < 3:
-            A.e(f"s_add_u32 {sr(S_TMP)}, {sr(S_TMP)}, 1024")
-    A.e(f"s_add_u32 {sr(ptr)}, {sr(ptr)}, %[tstride_lo]")
-    A.e(f"s_addc_u32 {sr(ptr + 1)}, {sr(ptr + 1)}, %[tstride_hi]")
-    A.e(f"{lbl_skip}:")
+            c.append(f"s_add_u32 {sr(S_TMP)}, {sr(S_TMP)}, 1024")
+        g.append(c)
+    g.append([f"s_add_u32 {sr(ptr)}, {sr(ptr)}, %[tstride_lo]",
+              f"s_addc_u32 {sr(ptr + 1)}, {sr(ptr + 1)}, %[tstride_hi]"])
+    return g
 
 
 def rotate(A, names, wrap_when):
@@ -299,6 +320,12 @@ def rotate(A, names, wrap_when):
         A.e(f"v_add_u32_e32 %[{n}], {sr(S_X)}, %[{n}]")
 
 
+def rotate_lines(names, wrap_when):
+    r = Lines()
+    rotate(r, names, wrap_when)
+    return r.lines
+
+
 KA = [f"ka{t}" for t in range(8)]
 VA = [f"va{d}" for d in range(4)]
 
@@ -306,23 +333,25 @@ VA = [f"va{d}" for d in range(4)]
 def half(A, parity, uid):
     cur, nxt = (V_SA, V_SB) if parity == 0 else (V_SB, V_SA)
     p = f"{parity}_{uid}"
-    dma(A, "k", f"Lnok{p}", 3, 0)        # K(t+3) -> buffer t mod 3 (held K(t), consumed)
-    dma(A, "v", f"Lnov{p}", 2, 2)        # V(t+2) -> buffer (t+2) mod 3 (held V(t-1), consumed)
-    rotate(A, VA, 0)                      # va: buffer (t-1) mod 3 -> t mod 3
+    # Scalar work of the tile, spread over the MFMA slots of phase A (copies, then the V address
+    # rotation, done before the first V read in slot 26) and phase B (the K address rotation,
+    # after the last K read of phase A):
+    #   K(t+3) -> buffer t mod 3 (held K(t), consumed); V(t+2) -> buffer (t+2) mod 3 (held V(t-1))
+    extra_a = dma_groups("k", 3, 0) + dma_groups("v", 2, 2) + [rotate_lines(VA, 0)]  # va: (t-1) -> t
+    extra_b = [rotate_lines(KA, 1)]                                                    # ka: (t+1) -> (t+2)
     A.e(f"s_add_u32 {sr(S_T1)}, {sr(S_T)}, 1")
     A.e(f"s_cmp_lt_u32 {sr(S_T1)}, %[nkt]")
     A.e(f"s_cbranch_scc0 Llast{p}")
     A.e(f"s_lshl_b32 {sr(S_KEY)}, {sr(S_T1)}, 6")
     A.e(f"s_cmp_ge_u32 {sr(S_T1)}, %[tmask]")
     A.e(f"s_cbranch_scc1 Lmask{p}")
-    block(A, cur, nxt, True, False)
+    block(A, cur, nxt, True, False, extra_a, extra_b)
     A.e(f"s_branch Lpost{p}")
     A.e(f"Lmask{p}:")
-    block(A, cur, nxt, True, True)
+    block(A, cur, nxt, True, True, extra_a, extra_b)
     A.e(f"Lpost{p}:")
     rescale(A, 0, f"Lnor0_{p}")
     rescale(A, 1, f"Lnor1_{p}")
-    rotate(A, KA, 1)                      # ka: buffer (t+1) mod 3 -> (t+2) mod 3
     A.e(f"s_add_u32 {sr(S_TMP)}, {sr(S_T)}, 2")
     A.e(f"s_cmp_lt_u32 {sr(S_TMP)}, %[nkt]")
     A.e(f"s_cbranch_scc0 Lnopre{p}")
@@ -338,6 +367,7 @@ def half(A, parity, uid):
 def last(A, parity, uid):
     cur, nxt = (V_SA, V_SB) if parity == 0 else (V_SB, V_SA)
     A.e(f"Llast{parity}_{uid}:")
+    rotate(A, VA, 0)                      # va: buffer (t-1) mod 3 -> t mod 3 (no copies remain)
     block(A, cur, nxt, False, False)
     A.e(f"s_branch Lend_{uid}")
 
