@@ -47,6 +47,7 @@ S_T, S_T1, S_KEY, S_ROWS, S_TMP, S_X = 80, 81, 82, 83, 84, 85
 S_KP, S_VP = 86, 88          # running 64-bit K / V tile pointers
 S_B0, S_Y = 90, 91           # S_B0 = t mod 3
 S_KR, S_VR = 92, 96          # buffer resource quads
+S_C = (82, 84)               # rescale-test lane masks of the row blocks (S_KEY/S_ROWS, S_TMP/S_X: free then)
 TILE_BYTES = 16384
 NBUF = 3
 
@@ -171,12 +172,13 @@ def block(A, cur, nxt, has_next, masked, extra_a=(), extra_b=()):
     for p, (qb, ks, m, a, b) in enumerate(pairs):  # row sums of S(t) (fp32 probabilities)
         slots_b[p] += [f"v_add_f32_e32 {vr(V_RS[qb])}, {vr(V_RS[qb])}, {vr(a)}",
                        f"v_add_f32_e32 {vr(V_RS[qb])}, {vr(V_RS[qb])}, {vr(b)}"]
-    if has_next:  # mask and row max of S(t+1): (qb, kb) blocks in the order their MFMAs finished
+    if has_next:  # mask and row max of S(t+1): (qb, kb) blocks in the order their MFMAs finished,
+        # in slots 0..23, so that the row-max exchange and the rescale test fit in slots 24..29
         order = [(0, 0), (1, 0), (0, 1), (1, 1)]
         first = {0: True, 1: True}
         for bi, (qb, kb) in enumerate(order):
             for r2 in range(8):
-                s = bi * 8 + r2
+                s = bi * 6 + (r2 * 6) // 8
                 ea = s_reg(nxt, qb, kb, 2 * r2)
                 eb = ea + 1
                 if masked:
@@ -189,6 +191,17 @@ def block(A, cur, nxt, has_next, masked, extra_a=(), extra_b=()):
                     first[qb] = False
                 else:
                     slots_b[s].append(f"v_max3_f32 {vr(V_MX[qb])}, {vr(V_MX[qb])}, {vr(ea)}, {vr(eb)}")
+        # Row max across the half-waves, then the rescale test (tile max above m_run + thr for any
+        # row of either block) into SCC; each step one slot after the one it reads, which covers
+        # the VALU -> permlane, permlane -> VALU and VALU-written SGPR -> SALU wait states.
+        # V_T0 (the mask bounds) is free after slot 23.
+        for qb in range(2):
+            slots_b[24].append(f"v_mov_b32 {vr(V_AL[qb])}, {vr(V_MX[qb])}")
+            slots_b[25].append(f"v_permlane32_swap_b32_e32 {vr(V_AL[qb])}, {vr(V_MX[qb])}")
+            slots_b[26].append(f"v_max_f32_e32 {vr(V_MX[qb])}, {vr(V_AL[qb])}, {vr(V_MX[qb])}")
+            slots_b[27].append(f"v_add_f32_e32 {vr(V_T0[qb])}, %[thr], %[mrun{qb}]")
+            slots_b[28].append(f"v_cmp_gt_f32_e64 {sr(S_C[qb], 2)}, {vr(V_MX[qb])}, {vr(V_T0[qb])}")
+        slots_b[29].append(f"s_or_b64 {sr(S_C[0], 2)}, {sr(S_C[0], 2)}, {sr(S_C[1], 2)}")  # SCC: any row
 
     A.e(f"v_mov_b32 {vr(V_RS[0])}, 0")
     A.e(f"v_mov_b32 {vr(V_RS[1])}, 0")
@@ -208,31 +221,29 @@ def block(A, cur, nxt, has_next, masked, extra_a=(), extra_b=()):
         for op in (extra_b[s] if s < len(extra_b) else []):
             A.e(op)
 
-    if has_next:
-        A.e("s_nop 1")
-        for qb in range(2):
-            A.e(f"v_mov_b32 {vr(V_AL[qb])}, {vr(V_MX[qb])}")
-        A.e("s_nop 1")
-        for qb in range(2):
-            A.e(f"v_permlane32_swap_b32_e32 {vr(V_AL[qb])}, {vr(V_MX[qb])}")
-        A.e("s_nop 1")
-        for qb in range(2):
-            A.e(f"v_max_f32_e32 {vr(V_MX[qb])}, {vr(V_AL[qb])}, {vr(V_MX[qb])}")
     for qb in range(2):
         A.e(f"v_add_f32_e32 %[lrun{qb}], %[lrun{qb}], {vr(V_RS[qb])}")
 
 
-def rescale(A, qb, lbl):
-    """Lazy running-max update of row block qb from its next-tile max, then its neg_mc."""
-    t0, al, mx = V_T0[qb], V_AL[qb], V_MX[qb]
-    A.e(f"v_add_f32_e32 {vr(t0)}, %[thr], %[mrun{qb}]")
-    A.e(f"v_cmp_gt_f32_e32 vcc, {vr(mx)}, {vr(t0)}")
-    A.e("s_nop 4")                                                        # VALU vcc -> vccz branch
-    A.e(f"s_cbranch_vccz {lbl}")
+def rescale_rows(A, p):
+    """After phase B: when the test of slot 29 found a row whose tile max exceeds its running max
+    by more than thr (rare), rescale the affected row blocks; otherwise fall through."""
+    A.e(f"s_cbranch_scc0 Lnoresc{p}")
     # O^T, written by the value product just before, is read by VALU below: >= 24 wait states
     A.e("s_nop 7")
     A.e("s_nop 7")
     A.e("s_nop 7")
+    rescale(A, 0, f"Lnor0_{p}")
+    rescale(A, 1, f"Lnor1_{p}")
+    A.e(f"Lnoresc{p}:")
+
+
+def rescale(A, qb, lbl):
+    """Lazy running-max update of row block qb (V_T0 holds m_run + thr), with its neg_mc."""
+    t0, al, mx = V_T0[qb], V_AL[qb], V_MX[qb]
+    A.e(f"v_cmp_gt_f32_e32 vcc, {vr(mx)}, {vr(t0)}")
+    A.e("s_nop 4")                                                        # VALU vcc -> vccz branch
+    A.e(f"s_cbranch_vccz {lbl}")
     A.e(f"v_cndmask_b32_e32 {vr(t0)}, %[mrun{qb}], {vr(mx)}, vcc")     # m_new
     A.e(f"v_sub_f32_e32 {vr(al)}, %[mrun{qb}], {vr(t0)}")
     A.e(f"v_mul_f32_e32 {vr(al)}, %[c], {vr(al)}")
@@ -249,11 +260,11 @@ def rescale(A, qb, lbl):
             A.e(f"v_mul_f32_e32 {vr(TMP_BASE + j)}, {vr(TMP_BASE + j)}, {vr(al)}")
         for j in range(N_TMP):
             A.e(f"v_accvgpr_write_b32 {ar(base + g + j)}, {vr(TMP_BASE + j)}")
-    A.e("s_nop 1")
-    A.e(f"{lbl}:")
-    A.e(f"v_mul_f32_e64 %[nmc{qb}], -%[mrun{qb}], %[c]")
+    A.e(f"v_mul_f32_e64 %[nmc{qb}], -%[mrun{qb}], %[c]")              # neg_mc follows m_run
     A.e(f"v_cmp_eq_f32_e32 vcc, 0xff800000, %[mrun{qb}]")
     A.e(f"v_cndmask_b32_e64 %[nmc{qb}], %[nmc{qb}], 0, vcc")
+    A.e("s_nop 1")
+    A.e(f"{lbl}:")
 
 
 class Lines:
@@ -350,8 +361,7 @@ def half(A, parity, uid):
     A.e(f"Lmask{p}:")
     block(A, cur, nxt, True, True, extra_a, extra_b)
     A.e(f"Lpost{p}:")
-    rescale(A, 0, f"Lnor0_{p}")
-    rescale(A, 1, f"Lnor1_{p}")
+    rescale_rows(A, p)
     A.e(f"s_add_u32 {sr(S_TMP)}, {sr(S_T)}, 2")
     A.e(f"s_cmp_lt_u32 {sr(S_TMP)}, %[nkt]")
     A.e(f"s_cbranch_scc0 Lnopre{p}")
