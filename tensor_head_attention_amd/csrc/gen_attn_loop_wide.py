@@ -100,6 +100,65 @@ def issue_v(A, j):
     return A.lds(f"ds_read_b64_tr_b16 {vr(base + 2, 2)}, %[va{db}] offset:{ks * 4096 + 2048}")
 
 
+# VALU issue cost in units of ~2.4 cycles: a wave64 v_exp_f32 ~12 cycles (5 units), other VALU
+# ~4.6 cycles (2 units), measured on the device with MFMA chains; one 32x32x16 MFMA lasts ~32
+# cycles (~13 units), the VALU budget of a slot.
+SLOT_BUDGET_A, SLOT_BUDGET_B = 13, 13
+
+
+def units(op):
+    if op.startswith("s_"):
+        return 0
+    return 5 if op.startswith("v_exp") else 2
+
+
+def pack(stream, fixed, budget, nslots=32):
+    """List-schedules a stream of VALU groups into the MFMA slots, after each slot's fixed ops.
+    Slot by slot, the ready group with the earliest deadline (then the earliest in the stream)
+    that fits in `budget` is placed; a group at its deadline is placed even over budget.  A group
+    is ready when the group it depends on sits at least one slot earlier (a transcendental result
+    read by VALU; a VALU result read by MFMA is covered by deadlines two slots early), and, for
+    groups marked ordered, when the previous ordered group is placed (the row sums keep their
+    accumulation order).
+    stream: list of (ops, deadline, dep, ordered) with dep the index of an earlier group, a 1-tuple
+    holding a slot fixed earlier, or None.  Returns the slots and the slot of each group."""
+    out = [list(f) for f in fixed]
+    load = [sum(units(o) for o in f) for f in fixed]
+    n = len(stream)
+    slot_of = [None] * n
+    ordered = [i for i in range(n) if stream[i][3]]
+    prev_ord = {ordered[k]: ordered[k - 1] for k in range(1, len(ordered))}
+    for sl in range(nslots):
+        while True:
+            best = None
+            for i, (ops, deadline, dep, _) in enumerate(stream):
+                if slot_of[i] is not None:
+                    continue
+                if isinstance(dep, int) and (slot_of[dep] is None or slot_of[dep] + 1 > sl):
+                    continue
+                if isinstance(dep, tuple) and dep[0] + 1 > sl:
+                    continue
+                if i in prev_ord and slot_of[prev_ord[i]] is None:
+                    continue
+                cost = sum(units(o) for o in ops)
+                if load[sl] + cost > budget and deadline > sl:
+                    continue
+                if best is None or (deadline, i) < (stream[best][1], best):
+                    best = i
+            if best is None:
+                break
+            slot_of[best] = sl
+            out[sl] += stream[best][0]
+            load[sl] += sum(units(o) for o in stream[best][0])
+    for i, (ops, deadline, dep, _) in enumerate(stream):
+        assert slot_of[i] is not None and slot_of[i] <= deadline, (ops, slot_of[i], deadline)
+    # emit each slot's groups in stream order (a group never precedes one it depends on)
+    for sl in range(nslots):
+        mine = sorted((i for i in range(n) if slot_of[i] == sl))
+        out[sl] = list(fixed[sl]) + [o for i in mine for o in stream[i][0]]
+    return out, slot_of
+
+
 def block(A, cur, nxt, has_next, masked, extra_a=(), extra_b=()):
     """One tile.  With has_next, K fragments 0..2 of tile t+1 are in flight at entry.
     extra_a / extra_b: groups of scalar-unit work (tile copies, buffer rotation) issued after the
@@ -130,15 +189,44 @@ def block(A, cur, nxt, has_next, masked, extra_a=(), extra_b=()):
         qb, ks, m, a, b = pairs[p]
         return f"v_cvt_pk_bf16_f32 {vr(V_P + 16 * qb + 4 * ks + m)}, {vr(a)}, {vr(b)}"
 
+    def softmax(p):
+        qb, ks, m, a, b = pairs[p]
+        return ([f"v_fma_f32 {vr(a)}, {vr(a)}, %[c], %[nmc{qb}]",
+                 f"v_fma_f32 {vr(b)}, {vr(b)}, %[c], %[nmc{qb}]"],
+                [f"v_exp_f32_e32 {vr(a)}, {vr(a)}"], [f"v_exp_f32_e32 {vr(b)}, {vr(b)}"])
+
+    def deadline_p(p):
+        """Last slot of phase B for the packing of pair p: two MFMAs before the value-product
+        slot 8ks + qb that reads it."""
+        qb, ks = pairs[p][0], pairs[p][1]
+        return 8 * ks + qb - 2
+
+    # Unmasked tiles split the softmax of S(t) between the phases so that both carry about the
+    # same VALU load: p = 2^(s*c + neg_mc) for pairs 0..N_A-1 and the bf16 packing of step
+    # ks = 0 in phase A; the remaining pairs, the other packings and the row sums in phase B.
+    # Masked tiles (the mask adds VALU work to phase B) keep the whole softmax in phase A.
+    balanced = has_next and not masked
+    N_A = 24 if balanced else 32
     slots_a = []
-    for p, (qb, ks, m, a, b) in enumerate(pairs):
-        ops = [f"v_fma_f32 {vr(a)}, {vr(a)}, %[c], %[nmc{qb}]",
-               f"v_fma_f32 {vr(b)}, {vr(b)}, %[c], %[nmc{qb}]",
-               f"v_exp_f32_e32 {vr(a)}, {vr(a)}",
-               f"v_exp_f32_e32 {vr(b)}, {vr(b)}"]
-        if p > 0:
-            ops.append(cvt(p - 1))  # the previous pair: its exp results are a slot old
-        slots_a.append(ops)
+    if balanced:
+        stream, exp_b = [], {}
+        for p in range(N_A):
+            f, ea, eb = softmax(p)
+            stream += [(f[:1], 31, None, False), (ea, 31, None, False), (f[1:], 31, None, False),
+                       (eb, 31, None, False)]
+            exp_b[p] = len(stream) - 1
+            if 1 <= p <= 8:       # the packing of the previous pair (read from phase-B slot 0 on)
+                stream.append(([cvt(p - 1)], 29, exp_b[p - 1], False))
+        slots_a, _ = pack(stream, [[] for _ in range(32)], SLOT_BUDGET_A)
+    else:
+        for p, (qb, ks, m, a, b) in enumerate(pairs):
+            ops = [f"v_fma_f32 {vr(a)}, {vr(a)}, %[c], %[nmc{qb}]",
+                   f"v_fma_f32 {vr(b)}, {vr(b)}, %[c], %[nmc{qb}]",
+                   f"v_exp_f32_e32 {vr(a)}, {vr(a)}",
+                   f"v_exp_f32_e32 {vr(b)}, {vr(b)}"]
+            if p > 0:
+                ops.append(cvt(p - 1))  # the previous pair: its exp results are a slot old
+            slots_a.append(ops)
 
     # ---- phase A ----
     if has_next:
@@ -169,9 +257,10 @@ def block(A, cur, nxt, has_next, masked, extra_a=(), extra_b=()):
 
     # ---- phase B ----
     slots_b = [[] for _ in range(32)]
-    for p, (qb, ks, m, a, b) in enumerate(pairs):  # row sums of S(t) (fp32 probabilities)
-        slots_b[p] += [f"v_add_f32_e32 {vr(V_RS[qb])}, {vr(V_RS[qb])}, {vr(a)}",
-                       f"v_add_f32_e32 {vr(V_RS[qb])}, {vr(V_RS[qb])}, {vr(b)}"]
+    if not balanced:
+        for p, (qb, ks, m, a, b) in enumerate(pairs):  # row sums of S(t) (fp32 probabilities)
+            slots_b[p] += [f"v_add_f32_e32 {vr(V_RS[qb])}, {vr(V_RS[qb])}, {vr(a)}",
+                           f"v_add_f32_e32 {vr(V_RS[qb])}, {vr(V_RS[qb])}, {vr(b)}"]
     if has_next:  # mask and row max of S(t+1): (qb, kb) blocks in the order their MFMAs finished,
         # in slots 0..23, so that the row-max exchange and the rescale test fit in slots 24..29
         order = [(0, 0), (1, 0), (0, 1), (1, 1)]
@@ -203,6 +292,28 @@ def block(A, cur, nxt, has_next, masked, extra_a=(), extra_b=()):
             slots_b[28].append(f"v_cmp_gt_f32_e64 {sr(S_C[qb], 2)}, {vr(V_MX[qb])}, {vr(V_T0[qb])}")
         slots_b[29].append(f"s_or_b64 {sr(S_C[0], 2)}, {sr(S_C[0], 2)}, {sr(S_C[1], 2)}")  # SCC: any row
 
+    if balanced:
+        # Flexible phase-B work, packed in order: the packings of P still missing (each at least
+        # two MFMAs before the value-product slot that reads it), the remaining softmax pairs and
+        # their packings, and the fp32 row sums in pair order (so the sums of each row block are
+        # those of the narrow kernel bit for bit).
+        stream, exp_b = [], {}
+        for dl in sorted({deadline_p(p) for p in range(8, 32)}):
+            group = [p for p in range(8, 32) if deadline_p(p) == dl]
+            for p in group:
+                if p >= N_A:
+                    f, ea, eb = softmax(p)
+                    stream += [(f[:1], dl - 1, None, False), (ea, dl - 1, None, False),
+                               (f[1:], dl - 1, None, False), (eb, dl - 1, None, False)]
+                    exp_b[p] = len(stream) - 1
+            for p in group:
+                stream.append(([cvt(p)], dl, exp_b.get(p), False))
+        # and the row sums, in pair order per row block (after the exps they read)
+        for p, (qb, ks, m, a, b) in enumerate(pairs):
+            stream.append(([f"v_add_f32_e32 {vr(V_RS[qb])}, {vr(V_RS[qb])}, {vr(a)}",
+                            f"v_add_f32_e32 {vr(V_RS[qb])}, {vr(V_RS[qb])}, {vr(b)}"], 31, exp_b.get(p), True))
+        slots_b, _ = pack(stream, slots_b, SLOT_BUDGET_B)
+
     A.e(f"v_mov_b32 {vr(V_RS[0])}, 0")
     A.e(f"v_mov_b32 {vr(V_RS[1])}, 0")
     for s in range(32):
@@ -214,7 +325,7 @@ def block(A, cur, nxt, has_next, masked, extra_a=(), extra_b=()):
             A.wait_for(v_ops[j])
         A.e(f"v_mfma_f32_32x32x16_bf16 {ar(A_O + 64 * qb + 16 * db, 16)}, {vr(V_VF + 4 * (j % 4), 4)}, "
             f"{vr(V_P + 16 * qb + 4 * ks, 4)}, {ar(A_O + 64 * qb + 16 * db, 16)}")
-        if s == 0:
+        if s == 0 and not balanced:
             A.e(cvt(31))  # last pair of P (read by the MFMAs of step ks = 3)
         for op in slots_b[s]:
             A.e(op)
