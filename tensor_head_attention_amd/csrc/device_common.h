@@ -120,6 +120,16 @@ __device__ __forceinline__ WorkItem work_item(int blk, int n_tiles, int BH, bool
   return {descending ? n_tiles - 1 - t : t, bh};
 }
 
+// Block order of the streaming kernels: workgroups reach the XCDs round-robin (blk % 8), and this
+// maps them so that XCD x takes the contiguous block range [x*q + min(x, r), ...) of a grid of
+// nb = 8q + r blocks.  Each XCD then streams its own contiguous share of the rows, and no cache line
+// of a row-indexed array (an lse vector read or written 4 bytes per row, the output) is shared by
+// the L2s of several XCDs.  A bijection on [0, nb); any order is correct.
+__device__ __forceinline__ uint32_t xcd_contiguous_block(uint32_t blk, uint32_t nb) {
+  const uint32_t q = nb / kXcds, r = nb % kXcds, x = blk % kXcds, slot = blk / kXcds;
+  return x * q + (x < r ? x : r) + slot;
+}
+
 // Round-to-nearest-even fp32 -> bf16 pair (the hardware conversion on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16x2 v = {(__bf16)a, (__bf16)b};

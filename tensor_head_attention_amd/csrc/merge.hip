@@ -6,8 +6,11 @@
 //   lse = M + log(sum_k w_k); all parts empty (-inf) -> o = 0, lse = -inf.
 //
 // HBM-bound streaming kernel: every partial is read once (non-temporal) and
-// the result written once.  See the two kernels below for how in-place use
-// stays race-free.
+// the result written once.  Blocks are spread so that each XCD takes a
+// contiguous eighth of the rows (xcd_contiguous_block): the lse vectors, read
+// and written 4 bytes per row, then have no cache line shared between XCDs,
+// which measured 29.4 -> 23.2 us for 8 fp32 partials [4096, 8, 128].  See the
+// two kernels below for how in-place use stays race-free.
 #include "device_common.h"
 #include "tha_kernels.h"
 
@@ -66,7 +69,8 @@ __global__ void __launch_bounds__(kThreads) merge_vec_kernel(PartPtrs parts, int
   constexpr int kChunk = 8;  // parts whose loads are in flight together
   const int lanes = 1 << lanes_log2;
   const int lane_in_row = threadIdx.x & (lanes - 1);
-  const int64_t row = (int64_t)blockIdx.x * (kThreads >> lanes_log2) + (threadIdx.x >> lanes_log2);
+  const int64_t row = (int64_t)xcd_contiguous_block(blockIdx.x, gridDim.x) * (kThreads >> lanes_log2) +
+                      (threadIdx.x >> lanes_log2);
   const bool live = row < rows;
   const int c = lane_in_row * 4;
   const int64_t off = row * D + c;
@@ -139,7 +143,8 @@ __global__ void __launch_bounds__(kThreads) merge_scalar_kernel(PartPtrs parts, 
                                                                int64_t rows, int S, int H, int D, int lanes_log2) {
   const int lanes = 1 << lanes_log2;
   const int lane_in_row = threadIdx.x & (lanes - 1);
-  const int64_t row = (int64_t)blockIdx.x * (kThreads >> lanes_log2) + (threadIdx.x >> lanes_log2);
+  const int64_t row = (int64_t)xcd_contiguous_block(blockIdx.x, gridDim.x) * (kThreads >> lanes_log2) +
+                      (threadIdx.x >> lanes_log2);
   if (row >= rows) return;  // whole rows leave together
   const int64_t bs = row / H;
   const int h = (int)(row - bs * H);
