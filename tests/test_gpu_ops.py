@@ -23,6 +23,8 @@ def _bits(t):
     (4, 1, 16, 8, 7, torch.int8),         # 1-byte elements
     (2, 3, 8, 4, 2, torch.float64),       # 8-byte elements
     (1, 1, 5, 2, 16, torch.bfloat16),     # P = 1 is a plain copy
+    (2, 2, 14, 4, 32, torch.bfloat16),    # odd shard length (7 tokens): plain visiting order
+    (3, 2, 18, 6, 24, torch.bfloat16),    # 96-byte runs (6 vectors, not a power of two), even/odd order
 ])
 def test_permute_and_unpermute_bit_exact(P, B, S, H, D, dtype):
     say(f"permute P{P} B{B} S{S} H{H} D{D} {dtype}")
