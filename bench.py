@@ -159,12 +159,13 @@ def main():
 
     # shard_permute alone, timed in batches of back-to-back calls: Q, K, V shards in turn, each
     # round on the next head group, so consecutive calls read distinct 64 MiB slices (24 x 64 MiB
-    # before one repeats, far more than the 256 MiB MALL): the reads come from HBM
-    # (into a buffer of their own: the step's grouped tensors feed the backward side figure)
+    # before one repeats, far more than the 256 MiB MALL), and write into 8 rotating 64 MiB
+    # outputs (512 MiB): neither the reads nor the writes can be served by the MALL
+    # (buffers of their own: the step's grouped tensors feed the backward side figure)
     names = ("q", "k", "v")
-    pout = torch.empty_like(grouped["q"])
-    pb = batch_times(torch, lambda i: T.shard_permute(shards[names[i % 3]], (i // 3) % P, out=pout))
-    del pout
+    pouts = [torch.empty_like(grouped["q"]) for _ in range(8)]
+    pb = batch_times(torch, lambda i: T.shard_permute(shards[names[i % 3]], (i // 3) % P, out=pouts[i % 8]))
+    del pouts
     components["shard_permute_batched"] = {"us_per_call": pb[len(pb) // 2] * 1e3, "us_min": pb[0] * 1e3,
                                            "timing": BATCH_NOTE,
                                            "GB_per_s": permute_bytes / (pb[len(pb) // 2] * 1e-3) / 1e9,
@@ -382,22 +383,24 @@ def config_side(T, W, torch, dev):
 
 def merge_rotating(T, torch, dev, n=8, S=4096, H=8, D=128, sets=3):
     """8-way attn_merge_lse at the Ring share's shape, cycling over 3 independent sets of fp32
-    partials (3 x 128 MiB > the 256 MB MALL), so every call reads its partials from HBM."""
+    partials (3 x 128 MiB > the 256 MB MALL) and 3 outputs, so every call reads its partials from
+    HBM."""
     g = torch.Generator(device=dev)
     g.manual_seed(11)
     parts = [([torch.randn((1, S, H, D), generator=g, device=dev) for _ in range(n)],
               [torch.randn((1, H, S), generator=g, device=dev) for _ in range(n)]) for _ in range(sets)]
-    out = torch.empty((1, S, H, D), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((1, H, S), dtype=torch.float32, device=dev)
+    outs = [(torch.empty((1, S, H, D), dtype=torch.bfloat16, device=dev),
+             torch.empty((1, H, S), dtype=torch.float32, device=dev)) for _ in range(sets)]
     for i in range(3):
-        T.attn_merge_lse(parts[i % sets][0], parts[i % sets][1], out=out, lse_out=lse)
-    per = batch_times(torch, lambda i: T.attn_merge_lse(parts[i % sets][0], parts[i % sets][1], out=out, lse_out=lse))
+        T.attn_merge_lse(parts[i % sets][0], parts[i % sets][1], out=outs[i % sets][0], lse_out=outs[i % sets][1])
+    per = batch_times(torch, lambda i: T.attn_merge_lse(parts[i % sets][0], parts[i % sets][1],
+                                                         out=outs[i % sets][0], lse_out=outs[i % sets][1]))
     ms = per[len(per) // 2]
     nbytes = n * (S * H * D * 4 + H * S * 4) + S * H * D * 2 + H * S * 4
     return {"attn_merge_lse_8way_hbm": {"us": ms * 1e3, "us_min": per[0] * 1e3, "timing": BATCH_NOTE,
                                         "bytes": nbytes, "GB_per_s": nbytes / (ms * 1e-3) / 1e9,
                                         "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                                        "inputs": f"{sets} rotating sets of {n} fp32 partials [1,{S},{H},{D}]"}}
+                                        "inputs": f"{sets} rotating sets of {n} fp32 partials [1,{S},{H},{D}] and outputs"}}
 
 
 def cpu_model():
