@@ -5,11 +5,15 @@ before compiling attn_bf16_d128.hip, which defines the operands and the C++ arou
 
 Per 64-key tile t, for a wavefront of 32 query rows (the kernel source explains the layout):
   phase A: S(t+1) = K(t+1) Q^T, 16 v_mfma_f32_32x32x16_bf16, each followed by a slice of the
-           softmax of tile t: p = 2^(s*c + neg_mc), the row sum, and the bf16 packing of P;
+           softmax of tile t: p = 2^(s*c + neg_mc), the row sum, and the bf16 packing of P, and
+           by one group of scalar work for the copies of K(t+2) and V(t+1) into LDS;
   phase B: O^T += V(t)^T P(t)^T, 16 MFMAs, each followed by a slice of the mask and row max of
-           tile t+1;
-  then the lazy running-max update, the copies of later tiles into LDS, and the barrier.
-Fragments are read from LDS three MFMAs ahead; each wait covers exactly the fragment needed.
+           tile t+1; in unmasked tiles the row max is complete by slot 7, and the exchange across
+           the half-waves, the running-sum update and the rescale test (into SCC) follow in slots
+           8..14;
+  then the lazy running-max update (a branch taken only when some row needs it) and the barrier.
+Fragments are read from LDS three MFMAs ahead (the first V fragments during the last slots of
+phase A); each wait covers exactly the fragment needed.
 The loop runs over nkt tiles starting at key tile tbase (0, or the second half of the key range
 when two wavefront groups of one workgroup split the keys); tmask counts from tbase.
 
@@ -21,7 +25,7 @@ Register map (physical VGPRs, pinned by the operand constraints):
   v31 row sum, v30 row max, v29 -inf, v28/v27 temporaries (the rescale also uses v[48:55]); s[80:99] scalar
   temporaries.
 Wait states: every VALU read of an MFMA result, and every MFMA read of a VALU result, is separated
-from the writer by at least eight MFMAs or three s_nop 7, so no hazard needs hardware interlocks.
+from the writer by at least two MFMAs or three s_nop 7, so no hazard needs hardware interlocks.
 """
 import sys
 
@@ -33,6 +37,7 @@ RS, MX, NEGINF, T0, ALPHA = 31, 30, 29, 28, 27
 S_T, S_T1, S_KEY, S_ROWS, S_TMP = 80, 81, 82, 83, 84
 S_KP, S_VP = 86, 88          # running 64-bit K/V tile pointers (pairs)
 S_KR, S_VR = 92, 96          # buffer resource quads (aligned)
+S_C = 82                     # rescale-test lane mask (pair; S_KEY/S_ROWS are free in phase B)
 TILE_BYTES = 16384
 
 
@@ -66,8 +71,9 @@ class Asm:
         self.e(f"s_waitcnt lgkmcnt({n})")
 
 
-def block(A, cur_base, nxt_base, kbuf, vbuf, has_next, mask_next):
-    """One tile: phase A (QK of tile t+1 || probabilities of tile t), phase B (PV of t || mask+max of t+1)."""
+def block(A, cur_base, nxt_base, kbuf, vbuf, has_next, mask_next, extra_a=()):
+    """One tile: phase A (QK of tile t+1 || probabilities of tile t), phase B (PV of t || mask+max of t+1).
+    extra_a: groups of scalar work (the tile copies) placed after the MFMAs of phase A."""
     A.lds_ops = 0
     A.e("s_waitcnt lgkmcnt(0)")
     A.e(f"v_mov_b32 {vr(RS)}, 0")
@@ -82,12 +88,19 @@ def block(A, cur_base, nxt_base, kbuf, vbuf, has_next, mask_next):
     def nxt(kb, r):
         return nxt_base + 16 * kb + r
 
-    k_ops = {}
+    k_ops, v_ops = {}, {}
 
     def issue_k(i):
         kb, tt = divmod(i, 8)
         off = kbuf * TILE_BYTES + kb * 8192
         k_ops[i] = A.lds(f"ds_read_b128 {vr(K_BASE + 4 * (i % 4), 4)}, %[ka{tt}] offset:{off}")
+
+    def issue_v(i):
+        ks, db = divmod(i, 4)
+        base = V_BASE + 4 * (i % 4)
+        off = vbuf * TILE_BYTES + ks * 4096
+        A.lds(f"ds_read_b64_tr_b16 {vr(base, 2)}, %[va{db}] offset:{off}")
+        v_ops[i] = A.lds(f"ds_read_b64_tr_b16 {vr(base + 2, 2)}, %[va{db}] offset:{off + 2048}")
 
     elems = [(kb, r) for kb in range(2) for r in range(16)]
     slots = []
@@ -116,6 +129,8 @@ def block(A, cur_base, nxt_base, kbuf, vbuf, has_next, mask_next):
         for i in range(16):
             if i + 3 < 16:
                 issue_k(i + 3)
+            else:
+                issue_v(i + 3 - 16)  # the first V fragments of phase B: V(t) is visible since the last barrier
             kb, tt = divmod(i, 8)
             A.wait_for(k_ops[i])
             src2 = "0" if tt == 0 else vr(nxt(kb, 0), 16)
@@ -123,39 +138,49 @@ def block(A, cur_base, nxt_base, kbuf, vbuf, has_next, mask_next):
                 f"{vr(Q_BASE + 4 * tt, 4)}, {src2}")
             for op in slots[i]:
                 A.e(op)
+            for op in (extra_a[i] if i < len(extra_a) else []):
+                A.e(op)
     else:
         for i in range(16):
             for op in slots[i]:
                 A.e(op)
-
-    v_ops = {}
-
-    def issue_v(i):
-        ks, db = divmod(i, 4)
-        base = V_BASE + 4 * (i % 4)
-        off = vbuf * TILE_BYTES + ks * 4096
-        A.lds(f"ds_read_b64_tr_b16 {vr(base, 2)}, %[va{db}] offset:{off}")
-        v_ops[i] = A.lds(f"ds_read_b64_tr_b16 {vr(base + 2, 2)}, %[va{db}] offset:{off + 2048}")
+        for i in range(3):
+            issue_v(i)
 
     bsl = [[] for _ in range(16)]
     if has_next:
-        for kb in range(2):
-            for r in range(16):
-                slot = kb * 8 + r // 2
-                e_ = nxt(kb, r)
-                if mask_next:
+        pairs = [(nxt(kb, r), nxt(kb, r + 1)) for kb in range(2) for r in range(0, 16, 2)]
+        if mask_next:
+            for kb in range(2):
+                for r in range(16):
+                    slot = kb * 8 + r // 2
+                    e_ = nxt(kb, r)
                     cconst = kb * 32 + (r >> 2) * 8 + (r & 3)
                     bsl[slot].append(f"v_cmp_ge_i32_e32 vcc, {cconst}, {vr(T0)}")
                     bsl[slot].append(f"v_cndmask_b32_e32 {vr(e_)}, {vr(e_)}, {vr(NEGINF)}, vcc")
-        pairs = [(nxt(kb, r), nxt(kb, r + 1)) for kb in range(2) for r in range(0, 16, 2)]
-        for pi, (ea, eb) in enumerate(pairs):
-            if pi == 0:
-                bsl[pi].append(f"v_max_f32_e32 {vr(MX)}, {vr(ea)}, {vr(eb)}")
-            else:
-                bsl[pi].append(f"v_max3_f32 {vr(MX)}, {vr(MX)}, {vr(ea)}, {vr(eb)}")
+            for pi, (ea, eb) in enumerate(pairs):
+                if pi == 0:
+                    bsl[pi].append(f"v_max_f32_e32 {vr(MX)}, {vr(ea)}, {vr(eb)}")
+                else:
+                    bsl[pi].append(f"v_max3_f32 {vr(MX)}, {vr(MX)}, {vr(ea)}, {vr(eb)}")
+        else:
+            # the row max of S(t+1) in slots 0..7 (block kb = 1, written by the last MFMA of phase A,
+            # from slot 4 on); then the exchange across the half-waves and the rescale test, each step
+            # one slot after the one it reads (VALU -> permlane, permlane -> VALU, VALU-written SGPR ->
+            # SALU); T0 ends as m_run + thr, which the rescale path reads.
+            for pi, (ea, eb) in enumerate(pairs):
+                if pi == 0:
+                    bsl[0].append(f"v_max_f32_e32 {vr(MX)}, {vr(ea)}, {vr(eb)}")
+                else:
+                    bsl[pi // 2].append(f"v_max3_f32 {vr(MX)}, {vr(MX)}, {vr(ea)}, {vr(eb)}")
+            bsl[8].append(f"v_mov_b32 {vr(T0)}, {vr(MX)}")
+            bsl[9].append(f"v_permlane32_swap_b32_e32 {vr(T0)}, {vr(MX)}")
+            bsl[10].append(f"v_max_f32_e32 {vr(MX)}, {vr(T0)}, {vr(MX)}")
+            bsl[11].append(f"v_add_f32_e32 {vr(T0)}, %[thr], %[mrun]")
+            bsl[12].append(f"v_cmp_gt_f32_e64 {sr(S_C, 2)}, {vr(MX)}, {vr(T0)}")
+            bsl[13].append(f"s_cmp_lg_u64 {sr(S_C, 2)}, 0")                  # SCC: some row rescales
+            bsl[14].append(f"v_add_f32_e32 %[lrun], %[lrun], {vr(RS)}")
 
-    for i in range(3):
-        issue_v(i)
     for i in range(16):
         if i + 3 < 16:
             issue_v(i + 3)
@@ -167,26 +192,32 @@ def block(A, cur_base, nxt_base, kbuf, vbuf, has_next, mask_next):
         for op in bsl[i]:
             A.e(op)
 
-    if has_next:
+    if has_next and mask_next:
         A.e("s_nop 1")
         A.e(f"v_mov_b32 {vr(T0)}, {vr(MX)}")
         A.e("s_nop 1")
         A.e(f"v_permlane32_swap_b32_e32 {vr(T0)}, {vr(MX)}")
         A.e("s_nop 1")
         A.e(f"v_max_f32_e32 {vr(MX)}, {vr(T0)}, {vr(MX)}")
-    A.e(f"v_add_f32_e32 %[lrun], %[lrun], {vr(RS)}")
-    # MFMA results (O) may be read by VALU right after: keep >= 24 wait states
-    A.e("s_nop 7")
-    A.e("s_nop 7")
-    A.e("s_nop 7")
+        A.e(f"v_add_f32_e32 %[lrun], %[lrun], {vr(RS)}")
+        A.e(f"v_add_f32_e32 {vr(T0)}, %[thr], %[mrun]")
+        A.e(f"v_cmp_gt_f32_e64 {sr(S_C, 2)}, {vr(MX)}, {vr(T0)}")
+        A.e("s_nop 4")
+        A.e(f"s_cmp_lg_u64 {sr(S_C, 2)}, 0")
+    elif not has_next:
+        A.e(f"v_add_f32_e32 %[lrun], %[lrun], {vr(RS)}")
 
 
 def rescale(A, lbl):
-    """Lazy running-max update from MX (row max of the next tile), then neg_mc."""
-    A.e(f"v_add_f32_e32 {vr(T0)}, %[thr], %[mrun]")
+    """After phase B, when the test found a row whose tile max exceeds m_run + thr (SCC set; rare):
+    raise the running max of those rows, rescale O^T and l_run, and follow with neg_mc.  T0 holds
+    m_run + thr and MX the row max of tile t+1."""
+    A.e(f"s_cbranch_scc0 {lbl}")
+    # O^T, written by the value product just before, is read by VALU below: >= 24 wait states
+    A.e("s_nop 7")
+    A.e("s_nop 7")
+    A.e("s_nop 7")
     A.e(f"v_cmp_gt_f32_e32 vcc, {vr(MX)}, {vr(T0)}")
-    A.e("s_nop 4")                                                       # vcc written by VALU -> vccz branch
-    A.e(f"s_cbranch_vccz {lbl}")
     A.e(f"v_cndmask_b32_e32 {vr(T0)}, %[mrun], {vr(MX)}, vcc")        # m_new
     A.e(f"v_sub_f32_e32 {vr(ALPHA)}, %[mrun], {vr(T0)}")
     A.e(f"v_mul_f32_e32 {vr(ALPHA)}, %[c], {vr(ALPHA)}")
@@ -203,39 +234,41 @@ def rescale(A, lbl):
             A.e(f"v_mul_f32_e32 {vr(TMP_BASE + j)}, {vr(TMP_BASE + j)}, {vr(ALPHA)}")
         for j in range(N_TMP):
             A.e(f"v_accvgpr_write_b32 {ar(O_AGPR + g + j)}, {vr(TMP_BASE + j)}")
-    A.e("s_nop 1")
-    A.e(f"{lbl}:")
-    A.e(f"v_mul_f32_e64 %[nmc], -%[mrun], %[c]")
+    A.e(f"v_mul_f32_e64 %[nmc], -%[mrun], %[c]")                      # neg_mc follows m_run
     A.e(f"v_cmp_eq_f32_e32 vcc, 0xff800000, %[mrun]")
     A.e(f"v_cndmask_b32_e64 %[nmc], %[nmc], 0, vcc")
+    A.e("s_nop 1")
+    A.e(f"{lbl}:")
 
 
-def dma(A, which, buf, lbl_skip, ahead):
-    """Copy tile (t + ahead) of K or V into LDS buffer `buf` if it exists; advances the running pointer."""
+def dma_groups(which, ahead, buf):
+    """Copy of tile t + ahead of K or V into LDS buffer `buf`, without branches: past this group's
+    last tile the copy has 0 valid rows (no memory is read; the buffer it fills is not read
+    again).  Returned as groups of scalar instructions, each placed after one MFMA of phase A;
+    every SCC producer sits next to its consumer inside a group."""
     ptr, rsrc, offs, dst = (S_KP, S_KR, "koff", "kdst") if which == "k" else (S_VP, S_VR, "voff", "vdst")
-    A.e(f"s_add_u32 {sr(S_TMP)}, {sr(S_T)}, {ahead}")
-    A.e(f"s_cmp_lt_u32 {sr(S_TMP)}, %[nkt]")
-    A.e(f"s_cbranch_scc0 {lbl_skip}")
-    # rows valid = min(64, kv_lim - 64*(t+ahead)); bytes = rows * row_bytes
-    A.e(f"s_add_u32 {sr(S_ROWS)}, {sr(S_TMP)}, %[tbase]")         # tile index in the key tensor
-    A.e(f"s_lshl_b32 {sr(S_ROWS)}, {sr(S_ROWS)}, 6")
-    A.e(f"s_sub_i32 {sr(S_ROWS)}, %[kvlim], {sr(S_ROWS)}")
-    A.e(f"s_min_i32 {sr(S_ROWS)}, {sr(S_ROWS)}, 64")
-    A.e(f"s_mul_i32 {sr(rsrc + 2)}, {sr(S_ROWS)}, %[rowb]")
-    A.e(f"s_mov_b32 {sr(rsrc)}, {sr(ptr)}")
-    A.e(f"s_and_b32 {sr(rsrc + 1)}, {sr(ptr + 1)}, 0xffff")
-    A.e(f"s_mov_b32 {sr(rsrc + 3)}, 0x20000")
-    A.e(f"s_add_u32 {sr(S_TMP)}, %[{dst}0], {buf * TILE_BYTES}")
+    g = []
+    g.append([f"s_add_u32 {sr(S_TMP)}, {sr(S_T)}, {ahead}",
+              f"s_add_u32 {sr(S_ROWS)}, {sr(S_TMP)}, %[tbase]",     # tile index in the key tensor
+              f"s_lshl_b32 {sr(S_ROWS)}, {sr(S_ROWS)}, 6",           # rows = min(64, kv_lim - 64 tile)
+              f"s_sub_i32 {sr(S_ROWS)}, %[kvlim], {sr(S_ROWS)}",
+              f"s_min_i32 {sr(S_ROWS)}, {sr(S_ROWS)}, 64",
+              f"s_max_i32 {sr(S_ROWS)}, {sr(S_ROWS)}, 0",
+              f"s_cmp_lt_u32 {sr(S_TMP)}, %[nkt]",                   # no such tile: 0 rows
+              f"s_cselect_b32 {sr(S_ROWS)}, {sr(S_ROWS)}, 0"])
+    g.append([f"s_mul_i32 {sr(rsrc + 2)}, {sr(S_ROWS)}, %[rowb]",
+              f"s_mov_b32 {sr(rsrc)}, {sr(ptr)}",
+              f"s_and_b32 {sr(rsrc + 1)}, {sr(ptr + 1)}, 0xffff",
+              f"s_mov_b32 {sr(rsrc + 3)}, 0x20000",
+              f"s_add_u32 {sr(S_TMP)}, %[{dst}0], {buf * TILE_BYTES}"])
     for u in range(4):
-        A.e(f"s_mov_b32 m0, {sr(S_TMP)}")
-        A.e("s_nop 0")
-        A.e(f"buffer_load_dwordx4 %[{offs}{u}], {sr(rsrc, 4)}, 0 offen lds")
+        c = [f"s_mov_b32 m0, {sr(S_TMP)}", "s_nop 0", f"buffer_load_dwordx4 %[{offs}{u}], {sr(rsrc, 4)}, 0 offen lds"]
         if u < 3:
-            A.e(f"s_add_u32 {sr(S_TMP)}, {sr(S_TMP)}, 1024")
-    # advance the running pointer by one tile
-    A.e(f"s_add_u32 {sr(ptr)}, {sr(ptr)}, %[tstride_lo]")
-    A.e(f"s_addc_u32 {sr(ptr + 1)}, {sr(ptr + 1)}, %[tstride_hi]")
-    A.e(f"{lbl_skip}:")
+            c.append(f"s_add_u32 {sr(S_TMP)}, {sr(S_TMP)}, 1024")
+        g.append(c)
+    g.append([f"s_add_u32 {sr(ptr)}, {sr(ptr)}, %[tstride_lo]",     # advance the running pointer
+              f"s_addc_u32 {sr(ptr + 1)}, {sr(ptr + 1)}, %[tstride_hi]"])
+    return g
 
 
 def half(A, parity, uid):
@@ -244,8 +277,9 @@ def half(A, parity, uid):
     kb_read = 1 - parity       # K buffer holding tile t+1
     vb_read = parity           # V buffer holding tile t
     p = f"{parity}_{uid}"
-    dma(A, "k", parity, f"Lnok{p}", 2)           # K(t+2) -> K buffer t&1
-    dma(A, "v", 1 - parity, f"Lnov{p}", 1)       # V(t+1) -> V buffer (t+1)&1
+    # K(t+2) -> K buffer t&1 (held K(t)), V(t+1) -> V buffer (t+1)&1 (held V(t-1)), both consumed
+    # before the last barrier; 7 + 7 groups over the 16 phase-A slots
+    extra_a = dma_groups("k", 2, parity) + [[]] + dma_groups("v", 1, 1 - parity)
     A.e(f"s_add_u32 {sr(S_T1)}, {sr(S_T)}, 1")
     A.e(f"s_cmp_lt_u32 {sr(S_T1)}, %[nkt]")
     A.e(f"s_cbranch_scc0 Llast{p}")
@@ -253,10 +287,10 @@ def half(A, parity, uid):
     A.e(f"s_lshl_b32 {sr(S_KEY)}, {sr(S_KEY)}, 6")
     A.e(f"s_cmp_ge_u32 {sr(S_T1)}, %[tmask]")
     A.e(f"s_cbranch_scc1 Lmask{p}")
-    block(A, cur_base, nxt_base, kb_read, vb_read, True, False)
+    block(A, cur_base, nxt_base, kb_read, vb_read, True, False, extra_a)
     A.e(f"s_branch Lpost{p}")
     A.e(f"Lmask{p}:")
-    block(A, cur_base, nxt_base, kb_read, vb_read, True, True)
+    block(A, cur_base, nxt_base, kb_read, vb_read, True, True, extra_a)
     A.e(f"Lpost{p}:")
     rescale(A, f"Lnorescale{p}")
     A.e("s_waitcnt vmcnt(0)")
@@ -291,6 +325,11 @@ def gen_loop():
     last(A, 0, uid)
     last(A, 1, uid)
     A.e(f"Lend_{uid}:")
+    # the code after the statement reads O^T, written by the last value-product MFMAs: >= 24 wait
+    # states (the compiler does not see the MFMAs inside the statement)
+    A.e("s_nop 7")
+    A.e("s_nop 7")
+    A.e("s_nop 7")
     return A.lines
 
 

@@ -515,6 +515,11 @@ def gen_loop():
     last(A, 0, uid)
     last(A, 1, uid)
     A.e(f"Lend_{uid}:")
+    # the code after the statement reads O^T, written by the last value-product MFMAs: >= 24 wait
+    # states (the compiler does not see the MFMAs inside the statement)
+    A.e("s_nop 7")
+    A.e("s_nop 7")
+    A.e("s_nop 7")
     return A.lines
 
 
