@@ -5,12 +5,16 @@ before compiling attn_bf16_d128.hip, which defines the operands and the C++ arou
 
 Per 64-key tile t, for a wavefront of 32 query rows (the kernel source explains the layout):
   phase A: S(t+1) = K(t+1) Q^T, 16 v_mfma_f32_32x32x16_bf16, each followed by a slice of the
-           softmax of tile t: p = 2^(s*c + neg_mc), the row sum, and the bf16 packing of P, and
-           by one group of scalar work for the copies of K(t+2) and V(t+1) into LDS;
+           softmax of tile t (p = 2^(s*c + neg_mc) and the bf16 packing of P into its own
+           registers) and by one group of scalar work for the copies of K(t+2) and V(t+1);
   phase B: O^T += V(t)^T P(t)^T, 16 MFMAs, each followed by a slice of the mask and row max of
            tile t+1; in unmasked tiles the row max is complete by slot 7, and the exchange across
-           the half-waves, the running-sum update and the rescale test (into SCC) follow in slots
-           8..14;
+           the half-waves and the rescale test (into SCC) follow in slots 8..13.
+  Unmasked tiles split the softmax between the phases with the list scheduler of the wide loop:
+  the exponentials of the first 12 pairs and the packing of the first 16-key step in phase A;
+  the other exponentials and packings (each two MFMAs before the value product that reads it)
+  and the fp32 row sums, in pair order, in phase B.  Masked tiles keep the whole softmax and the
+  row sums in phase A (the mask adds VALU work to phase B).
   then the lazy running-max update (a branch taken only when some row needs it) and the barrier.
 Fragments are read from LDS three MFMAs ahead (the first V fragments during the last slots of
 phase A); each wait covers exactly the fragment needed.
@@ -21,6 +25,7 @@ Register map (physical VGPRs, pinned by the operand constraints):
   O^T[db]   a[16db : 16db+15]           (fp32 accumulators in AGPRs, 4 blocks of 32 dims)
   S set A   v[128:159], S set B v[96:127] (scores of the current / next tile, alternating)
   Q^T[t]    v[64+4t : 67+4t]            (bf16 fragments, loaded once)
+  P(ks)     v[160+4ks : 163+4ks]        (bf16 probabilities of the current tile, 16 keys per step)
   K frags   v[48:63], V frags v[32:47]   (rotating prefetch buffers)
   v31 row sum, v30 row max, v29 -inf, v28/v27 temporaries (the rescale also uses v[48:55]); s[80:99] scalar
   temporaries.
@@ -29,7 +34,10 @@ from the writer by at least two MFMAs or three s_nop 7, so no hazard needs hardw
 """
 import sys
 
+from gen_attn_loop_wide import pack  # the list scheduler that fills MFMA slots with VALU groups
+
 SA_BASE, SB_BASE, Q_BASE, K_BASE, V_BASE = 128, 96, 64, 48, 32
+P_BASE = 160                 # bf16 probabilities of the current tile: P(ks) in v[160 + 4ks : +3]
 O_AGPR = 0                   # O^T accumulators in a[0:63]
 TMP_BASE, N_TMP = 48, 8      # rescale temporaries: the K fragment buffers, idle at that point
 RS, MX, NEGINF, T0, ALPHA = 31, 30, 29, 28, 27
@@ -39,6 +47,8 @@ S_KP, S_VP = 86, 88          # running 64-bit K/V tile pointers (pairs)
 S_KR, S_VR = 92, 96          # buffer resource quads (aligned)
 S_C = 82                     # rescale-test lane mask (pair; S_KEY/S_ROWS are free in phase B)
 TILE_BYTES = 16384
+SLOT_BUDGET = 13             # VALU issue units per MFMA slot (v_exp 5, other VALU 2; see the wide loop)
+N_A = 12                     # softmax pairs of an unmasked tile whose FMA/exp run in phase A
 
 
 def vr(a, n=1):
@@ -102,26 +112,43 @@ def block(A, cur_base, nxt_base, kbuf, vbuf, has_next, mask_next, extra_a=()):
         A.lds(f"ds_read_b64_tr_b16 {vr(base, 2)}, %[va{db}] offset:{off}")
         v_ops[i] = A.lds(f"ds_read_b64_tr_b16 {vr(base + 2, 2)}, %[va{db}] offset:{off + 2048}")
 
-    elems = [(kb, r) for kb in range(2) for r in range(16)]
-    slots = []
-    for i in range(16):
-        (ka, ra), (kb_, rb) = elems[2 * i], elems[2 * i + 1]
-        ea, eb = cur(ka, ra), cur(kb_, rb)
-        slots.append([
-            f"v_fma_f32 {vr(ea)}, {vr(ea)}, %[c], %[nmc]",
-            f"v_fma_f32 {vr(eb)}, {vr(eb)}, %[c], %[nmc]",
-            f"v_exp_f32_e32 {vr(ea)}, {vr(ea)}",
-            f"v_exp_f32_e32 {vr(eb)}, {vr(eb)}",
-            f"v_add_f32_e32 {vr(RS)}, {vr(RS)}, {vr(ea)}",
-            f"v_add_f32_e32 {vr(RS)}, {vr(RS)}, {vr(eb)}",
-        ])
-    for g in range(4):
-        kb, h = divmod(g, 2)
-        for m in range(4):
-            d = cur(kb, 8 * h + m)
-            s0, s1 = cur(kb, 8 * h + 2 * m), cur(kb, 8 * h + 2 * m + 1)
-            slot = min(4 * g + 4 + m, 15)
-            slots[slot].append(f"v_cvt_pk_bf16_f32 {vr(d)}, {vr(s0)}, {vr(s1)}")
+    # pair p = 4ks + m: elements r = 8h + 2m, r + 1 of score block kb (ks = 2kb + h); the pairs
+    # in this order are also the row-sum order
+    pairs = []
+    for p in range(16):
+        ks, m = divmod(p, 4)
+        kb, h = divmod(ks, 2)
+        a = cur(kb, 8 * h + 2 * m)
+        pairs.append((ks, m, a, a + 1))
+
+    def cvt(p):
+        ks, m, a, b = pairs[p]
+        return f"v_cvt_pk_bf16_f32 {vr(P_BASE + 4 * ks + m)}, {vr(a)}, {vr(b)}"
+
+    def rowsum(p):
+        ks, m, a, b = pairs[p]
+        return [f"v_add_f32_e32 {vr(RS)}, {vr(RS)}, {vr(a)}", f"v_add_f32_e32 {vr(RS)}, {vr(RS)}, {vr(b)}"]
+
+    def softmax(p):
+        ks, m, a, b = pairs[p]
+        return ([f"v_fma_f32 {vr(a)}, {vr(a)}, %[c], %[nmc]"], [f"v_exp_f32_e32 {vr(a)}, {vr(a)}"],
+                [f"v_fma_f32 {vr(b)}, {vr(b)}, %[c], %[nmc]"], [f"v_exp_f32_e32 {vr(b)}, {vr(b)}"])
+
+    balanced = has_next and not mask_next
+    if balanced:
+        stream = []
+        for p in range(N_A):
+            stream += [(g, 15, None, False) for g in softmax(p)]
+            if p < 4:  # the first 16-key step of P: read by the first value-product MFMA
+                stream.append(([cvt(p)], 13, len(stream) - 1, False))
+        slots, _ = pack(stream, [[] for _ in range(16)], SLOT_BUDGET, nslots=16)
+    else:
+        slots = []
+        for p in range(16):
+            f, ea, fb, eb = softmax(p)
+            slots.append(f + fb + ea + eb + rowsum(p))
+        for p in range(16):  # packing one slot after its exponentials (transcendental -> VALU)
+            slots[min(p + 1, 15)].append(cvt(p))
 
     if has_next:
         for i in range(3):
@@ -149,7 +176,7 @@ def block(A, cur_base, nxt_base, kbuf, vbuf, has_next, mask_next, extra_a=()):
 
     bsl = [[] for _ in range(16)]
     if has_next:
-        pairs = [(nxt(kb, r), nxt(kb, r + 1)) for kb in range(2) for r in range(0, 16, 2)]
+        mpairs = [(nxt(kb, r), nxt(kb, r + 1)) for kb in range(2) for r in range(0, 16, 2)]
         if mask_next:
             for kb in range(2):
                 for r in range(16):
@@ -158,7 +185,7 @@ def block(A, cur_base, nxt_base, kbuf, vbuf, has_next, mask_next, extra_a=()):
                     cconst = kb * 32 + (r >> 2) * 8 + (r & 3)
                     bsl[slot].append(f"v_cmp_ge_i32_e32 vcc, {cconst}, {vr(T0)}")
                     bsl[slot].append(f"v_cndmask_b32_e32 {vr(e_)}, {vr(e_)}, {vr(NEGINF)}, vcc")
-            for pi, (ea, eb) in enumerate(pairs):
+            for pi, (ea, eb) in enumerate(mpairs):
                 if pi == 0:
                     bsl[pi].append(f"v_max_f32_e32 {vr(MX)}, {vr(ea)}, {vr(eb)}")
                 else:
@@ -168,7 +195,7 @@ def block(A, cur_base, nxt_base, kbuf, vbuf, has_next, mask_next, extra_a=()):
             # from slot 4 on); then the exchange across the half-waves and the rescale test, each step
             # one slot after the one it reads (VALU -> permlane, permlane -> VALU, VALU-written SGPR ->
             # SALU); T0 ends as m_run + thr, which the rescale path reads.
-            for pi, (ea, eb) in enumerate(pairs):
+            for pi, (ea, eb) in enumerate(mpairs):
                 if pi == 0:
                     bsl[0].append(f"v_max_f32_e32 {vr(MX)}, {vr(ea)}, {vr(eb)}")
                 else:
@@ -179,7 +206,20 @@ def block(A, cur_base, nxt_base, kbuf, vbuf, has_next, mask_next, extra_a=()):
             bsl[11].append(f"v_add_f32_e32 {vr(T0)}, %[thr], %[mrun]")
             bsl[12].append(f"v_cmp_gt_f32_e64 {sr(S_C, 2)}, {vr(MX)}, {vr(T0)}")
             bsl[13].append(f"s_cmp_lg_u64 {sr(S_C, 2)}, 0")                  # SCC: some row rescales
-            bsl[14].append(f"v_add_f32_e32 %[lrun], %[lrun], {vr(RS)}")
+            # the rest of the softmax of tile t: exponentials of pairs N_A.. and packings (each
+            # two MFMAs before the value product that reads it), then the row sums in pair order
+            stream, exp_b, cvt_dep = [], {}, {}
+            for ks in range(1, 4):
+                dl = 4 * ks - 2
+                for p in range(4 * ks, 4 * ks + 4):
+                    if p >= N_A:
+                        stream += [(g, dl - 1, None, False) for g in softmax(p)]
+                        exp_b[p] = len(stream) - 1
+                for p in range(4 * ks, 4 * ks + 4):
+                    stream.append(([cvt(p)], dl, exp_b.get(p), False))
+            for p in range(16):
+                stream.append((rowsum(p), 15, exp_b.get(p), True))
+            bsl, _ = pack(stream, bsl, SLOT_BUDGET, nslots=16)
 
     for i in range(16):
         if i + 3 < 16:
@@ -188,7 +228,7 @@ def block(A, cur_base, nxt_base, kbuf, vbuf, has_next, mask_next, extra_a=()):
         kb, h = divmod(ks, 2)
         A.wait_for(v_ops[i])
         A.e(f"v_mfma_f32_32x32x16_bf16 {ar(O_AGPR + 16 * db, 16)}, {vr(V_BASE + 4 * (i % 4), 4)}, "
-            f"{vr(cur(kb, 8 * h), 4)}, {ar(O_AGPR + 16 * db, 16)}")
+            f"{vr(P_BASE + 4 * ks, 4)}, {ar(O_AGPR + 16 * db, 16)}")
         for op in bsl[i]:
             A.e(op)
 
@@ -199,13 +239,11 @@ def block(A, cur_base, nxt_base, kbuf, vbuf, has_next, mask_next, extra_a=()):
         A.e(f"v_permlane32_swap_b32_e32 {vr(T0)}, {vr(MX)}")
         A.e("s_nop 1")
         A.e(f"v_max_f32_e32 {vr(MX)}, {vr(T0)}, {vr(MX)}")
-        A.e(f"v_add_f32_e32 %[lrun], %[lrun], {vr(RS)}")
         A.e(f"v_add_f32_e32 {vr(T0)}, %[thr], %[mrun]")
         A.e(f"v_cmp_gt_f32_e64 {sr(S_C, 2)}, {vr(MX)}, {vr(T0)}")
         A.e("s_nop 4")
         A.e(f"s_cmp_lg_u64 {sr(S_C, 2)}, 0")
-    elif not has_next:
-        A.e(f"v_add_f32_e32 %[lrun], %[lrun], {vr(RS)}")
+    A.e(f"v_add_f32_e32 %[lrun], %[lrun], {vr(RS)}")
 
 
 def rescale(A, lbl):
@@ -335,7 +373,7 @@ def gen_loop():
 
 # Registers the loop writes besides its own "+v" operands: pinned accumulator / score sets and
 # the clobber list.  No input operand may be allocated inside these.
-WRITTEN_VGPRS = set(range(27, 64)) | set(range(96, 160)) | set(range(TMP_BASE, TMP_BASE + N_TMP))
+WRITTEN_VGPRS = set(range(27, 64)) | set(range(96, 176)) | set(range(TMP_BASE, TMP_BASE + N_TMP))
 WRITTEN_SGPRS = set(range(80, 100))
 WRITTEN_AGPRS = set(range(O_AGPR, O_AGPR + 64))
 READ_WRITE_OPERANDS = ("mrun", "lrun", "nmc")
@@ -403,6 +441,7 @@ def main(out):
     lines = gen_loop()
     vclob = [f"v{i}" for i in range(V_BASE, V_BASE + 32)] + [f"v{i}" for i in (RS, MX, NEGINF, T0, ALPHA)]
     vclob += [f"v{i}" for i in range(TMP_BASE, TMP_BASE + N_TMP)]
+    vclob += [f"v{i}" for i in range(P_BASE, P_BASE + 16)]
     sclob = [f"s{i}" for i in range(80, 100)]
     clob = ", ".join('"%s"' % c for c in vclob + sclob + ["vcc", "scc", "m0", "memory"])
     body = "".join('      "%s\\n\\t" \\\n' % l for l in lines)
