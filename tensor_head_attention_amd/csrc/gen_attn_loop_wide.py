@@ -11,10 +11,12 @@ Per 64-key tile t, for a wavefront of 64 query rows (two 32-row blocks qb = 0, 1
   phase B: O^T += V(t)^T P(t)^T, 32 MFMAs (each V fragment feeds both row blocks), each followed
            by a slice of the row sums of tile t (fp32) and of the mask and row max of tile t+1;
   then the lazy running-max update and the barrier.
-K and V tiles are triple buffered in LDS: the copies of K(t+3) and V(t+2) are issued at the start
-of block t, and the first K fragments of the next block are read before the barrier that ends this
-one, so no LDS read ever waits behind a barrier.  Fragment reads run three fragments (six MFMAs)
-ahead; each wait covers exactly the fragment needed.
+K tiles live in four LDS buffers (tile t in buffer t mod 4) and V tiles in two (t mod 2), and the
+loop is unrolled four times, so every LDS read and copy destination is a fixed offset (no address
+arithmetic per tile).  Block t copies K(t+3) and V(t+1); the first K fragments of the next block
+are read before the barrier that ends this one (K(t+2) is visible since the previous barrier), so
+no LDS read waits behind a barrier.  Fragment reads run three fragments (six MFMAs) ahead; each
+wait covers exactly the fragment needed.
 
 Register map (pinned by the operand constraints):
   O^T[qb][db]  a[64qb + 16db : +15]       fp32 accumulators (AGPRs)
@@ -24,6 +26,7 @@ Register map (pinned by the operand constraints):
   P[qb][ks]    v[64 + 16qb + 4ks : +3]    bf16 probabilities of the current tile
   v[54:63]     row max / mask bound / alpha / row sum per row block, -inf, a temporary
   s[80:99]     scalar temporaries
+LDS: K buffers 0..3 at 16 KiB steps from %[ka*]'s base, V buffers 0..1 from %[va*]'s base.
 Wait states: VALU reads of MFMA results and MFMA reads of VALU results are separated by at least
 two MFMAs; before O^T is read by VALU the loop issues three s_nop 7.
 """
@@ -45,11 +48,11 @@ TMP_BASE, N_TMP = V_VF, 8   # rescale temporaries: the V fragment buffers, idle 
 
 S_T, S_T1, S_KEY, S_ROWS, S_TMP, S_X = 80, 81, 82, 83, 84, 85
 S_KP, S_VP = 86, 88          # running 64-bit K / V tile pointers
-S_B0, S_Y = 90, 91           # S_B0 = t mod 3
+S_Y = 91
 S_KR, S_VR = 92, 96          # buffer resource quads
 S_C = (82, 84)               # rescale-test lane masks of the row blocks (S_KEY/S_ROWS, S_TMP/S_X: free then)
 TILE_BYTES = 16384
-NBUF = 3
+NKBUF, NVBUF = 4, 2          # K and V LDS buffers; the loop is unrolled NKBUF times
 
 
 def vr(a, n=1):
@@ -86,18 +89,19 @@ def s_reg(base, qb, kb, r=0):
     return base + 32 * qb + 16 * kb + r
 
 
-def issue_k(A, i):
-    """K fragment i (kb = i // 8, dims 16tt..: tt = i % 8) of the tile ka points at."""
+def issue_k(A, i, kbuf):
+    """K fragment i (kb = i // 8, dims 16tt..: tt = i % 8) of the tile in K buffer kbuf."""
     kb, tt = divmod(i, 8)
-    return A.lds(f"ds_read_b128 {vr(V_KF + 4 * (i % 4), 4)}, %[ka{tt}] offset:{kb * 8192}")
+    return A.lds(f"ds_read_b128 {vr(V_KF + 4 * (i % 4), 4)}, %[ka{tt}] offset:{kbuf * TILE_BYTES + kb * 8192}")
 
 
-def issue_v(A, j):
-    """V fragment j (16-key step ks = j // 4, 32-dim block db = j % 4) of the tile va points at."""
+def issue_v(A, j, vbuf):
+    """V fragment j (16-key step ks = j // 4, 32-dim block db = j % 4) of the tile in V buffer vbuf."""
     ks, db = divmod(j, 4)
     base = V_VF + 4 * (j % 4)
-    A.lds(f"ds_read_b64_tr_b16 {vr(base, 2)}, %[va{db}] offset:{ks * 4096}")
-    return A.lds(f"ds_read_b64_tr_b16 {vr(base + 2, 2)}, %[va{db}] offset:{ks * 4096 + 2048}")
+    off = vbuf * TILE_BYTES + ks * 4096
+    A.lds(f"ds_read_b64_tr_b16 {vr(base, 2)}, %[va{db}] offset:{off}")
+    return A.lds(f"ds_read_b64_tr_b16 {vr(base + 2, 2)}, %[va{db}] offset:{off + 2048}")
 
 
 # VALU issue cost in units of ~2.4 cycles: a wave64 v_exp_f32 ~12 cycles (5 units), other VALU
@@ -159,8 +163,9 @@ def pack(stream, fixed, budget, nslots=32):
     return out, slot_of
 
 
-def block(A, cur, nxt, has_next, masked, extra_a=(), extra_b=()):
-    """One tile.  With has_next, K fragments 0..2 of tile t+1 are in flight at entry.
+def block(A, cur, nxt, has_next, masked, kbuf, vbuf, extra_a=(), extra_b=()):
+    """One tile t.  kbuf: K buffer of tile t+1; vbuf: V buffer of tile t.  With has_next, K
+    fragments 0..2 of tile t+1 are in flight at entry.
     extra_a / extra_b: groups of scalar-unit work (tile copies, buffer rotation) issued after the
     MFMA of slot i of phase A / B, so they run in the shadow of the matrix core."""
     A.n_ops = 0
@@ -235,10 +240,10 @@ def block(A, cur, nxt, has_next, masked, extra_a=(), extra_b=()):
             kb, tt = divmod(i, 8)
             if qb == 0:
                 if i + 3 < 16:
-                    k_ops[i + 3] = issue_k(A, i + 3)
+                    k_ops[i + 3] = issue_k(A, i + 3, kbuf)
                 else:
                     jv = i + 3 - 16
-                    v_ops[jv] = issue_v(A, jv)
+                    v_ops[jv] = issue_v(A, jv, vbuf)
                 A.wait_for(k_ops[i])
             dst = s_reg(nxt, qb, kb)
             src2 = "0" if tt == 0 else vr(dst, 16)
@@ -250,7 +255,7 @@ def block(A, cur, nxt, has_next, masked, extra_a=(), extra_b=()):
                 A.e(op)
     else:
         for jv in range(3):
-            v_ops[jv] = issue_v(A, jv)
+            v_ops[jv] = issue_v(A, jv, vbuf)
         for s in range(32):
             for op in slots_a[s]:
                 A.e(op)
@@ -321,7 +326,7 @@ def block(A, cur, nxt, has_next, masked, extra_a=(), extra_b=()):
         ks, db = divmod(j, 4)
         if qb == 0:
             if j + 3 < 16:
-                v_ops[j + 3] = issue_v(A, j + 3)
+                v_ops[j + 3] = issue_v(A, j + 3, vbuf)
             A.wait_for(v_ops[j])
         A.e(f"v_mfma_f32_32x32x16_bf16 {ar(A_O + 64 * qb + 16 * db, 16)}, {vr(V_VF + 4 * (j % 4), 4)}, "
             f"{vr(V_P + 16 * qb + 4 * ks, 4)}, {ar(A_O + 64 * qb + 16 * db, 16)}")
@@ -387,19 +392,8 @@ class Lines:
         self.lines.append(s)
 
 
-def buf_index(A, dst, add):
-    """dst = (S_B0 + add) mod 3."""
-    if add == 0:
-        A.e(f"s_mov_b32 {sr(dst)}, {sr(S_B0)}")
-        return
-    A.e(f"s_add_u32 {sr(dst)}, {sr(S_B0)}, {add}")
-    A.e(f"s_sub_u32 {sr(S_Y)}, {sr(dst)}, {NBUF}")
-    A.e(f"s_cmp_ge_u32 {sr(dst)}, {NBUF}")
-    A.e(f"s_cselect_b32 {sr(dst)}, {sr(S_Y)}, {sr(dst)}")
-
-
-def dma_groups(which, ahead, buf_add):
-    """Copy of tile t + ahead of K or V into LDS buffer (t + buf_add) mod 3, without branches:
+def dma_groups(which, ahead, buf):
+    """Copy of tile t + ahead of K or V into LDS buffer `buf`, without branches:
     past the last tile the copy has 0 valid rows (no memory is read; the buffer it fills is not
     read again).  Returned as groups of instructions, each group placed after one MFMA; every
     SCC producer sits next to its consumer inside a group."""
@@ -416,11 +410,7 @@ def dma_groups(which, ahead, buf_add):
               f"s_mov_b32 {sr(rsrc)}, {sr(ptr)}",
               f"s_and_b32 {sr(rsrc + 1)}, {sr(ptr + 1)}, 0xffff",
               f"s_mov_b32 {sr(rsrc + 3)}, 0x20000"])
-    b = Lines()
-    buf_index(b, S_X, buf_add)
-    b.e(f"s_lshl_b32 {sr(S_X)}, {sr(S_X)}, 14")
-    b.e(f"s_add_u32 {sr(S_TMP)}, %[{dst}0], {sr(S_X)}")
-    g.append(b.lines)
+    g[-1].append(f"s_add_u32 {sr(S_TMP)}, %[{dst}0], {buf * TILE_BYTES}")
     for u in range(4):
         c = [f"s_mov_b32 m0, {sr(S_TMP)}", "s_nop 0", f"buffer_load_dwordx4 %[{offs}{u}], {sr(rsrc, 4)}, 0 offen lds"]
         if u < 3:
@@ -431,65 +421,45 @@ def dma_groups(which, ahead, buf_add):
     return g
 
 
-def rotate(A, names, wrap_when):
-    """Move LDS read addresses to the next buffer: +16 KiB, or back from buffer 2 to 0 when
-    S_B0 == wrap_when."""
-    A.e(f"s_mov_b32 {sr(S_X)}, 0x4000")                        # +16 KiB
-    A.e(f"s_mov_b32 {sr(S_Y)}, 0xffff8000")                    # -32 KiB
-    A.e(f"s_cmp_eq_u32 {sr(S_B0)}, {wrap_when}")
-    A.e(f"s_cselect_b32 {sr(S_X)}, {sr(S_Y)}, {sr(S_X)}")
-    for n in names:
-        A.e(f"v_add_u32_e32 %[{n}], {sr(S_X)}, %[{n}]")
-
-
-def rotate_lines(names, wrap_when):
-    r = Lines()
-    rotate(r, names, wrap_when)
-    return r.lines
-
-
 KA = [f"ka{t}" for t in range(8)]
 VA = [f"va{d}" for d in range(4)]
 
 
-def half(A, parity, uid):
-    cur, nxt = (V_SA, V_SB) if parity == 0 else (V_SB, V_SA)
-    p = f"{parity}_{uid}"
-    # Scalar work of the tile, spread over the MFMA slots of phase A (copies, then the V address
-    # rotation, done before the first V read in slot 26) and phase B (the K address rotation,
-    # after the last K read of phase A):
-    #   K(t+3) -> buffer t mod 3 (held K(t), consumed); V(t+2) -> buffer (t+2) mod 3 (held V(t-1))
-    extra_a = dma_groups("k", 3, 0) + dma_groups("v", 2, 2) + [rotate_lines(VA, 0)]  # va: (t-1) -> t
-    extra_b = [rotate_lines(KA, 1)]                                                    # ka: (t+1) -> (t+2)
+def half(A, u, uid):
+    """Tile t with t mod 4 == u (when t + 1 < nkt; else the last block)."""
+    cur, nxt = (V_SA, V_SB) if u % 2 == 0 else (V_SB, V_SA)
+    p = f"{u}_{uid}"
+    # Scalar work of the tile, spread over the MFMA slots of phase A: K(t+3) -> K buffer (t+3) mod 4
+    # (held K(t-1), consumed two barriers ago), V(t+1) -> V buffer (t+1) mod 2 (held V(t-1),
+    # consumed before the last barrier)
+    extra_a = dma_groups("k", 3, (u + 3) % NKBUF) + dma_groups("v", 1, (u + 1) % NVBUF)
     A.e(f"s_add_u32 {sr(S_T1)}, {sr(S_T)}, 1")
     A.e(f"s_cmp_lt_u32 {sr(S_T1)}, %[nkt]")
     A.e(f"s_cbranch_scc0 Llast{p}")
     A.e(f"s_lshl_b32 {sr(S_KEY)}, {sr(S_T1)}, 6")
     A.e(f"s_cmp_ge_u32 {sr(S_T1)}, %[tmask]")
     A.e(f"s_cbranch_scc1 Lmask{p}")
-    block(A, cur, nxt, True, False, extra_a, extra_b)
+    block(A, cur, nxt, True, False, (u + 1) % NKBUF, u % NVBUF, extra_a)
     A.e(f"s_branch Lpost{p}")
     A.e(f"Lmask{p}:")
-    block(A, cur, nxt, True, True, extra_a, extra_b)
+    block(A, cur, nxt, True, True, (u + 1) % NKBUF, u % NVBUF, extra_a)
     A.e(f"Lpost{p}:")
     rescale_rows(A, p)
     A.e(f"s_add_u32 {sr(S_TMP)}, {sr(S_T)}, 2")
     A.e(f"s_cmp_lt_u32 {sr(S_TMP)}, %[nkt]")
     A.e(f"s_cbranch_scc0 Lnopre{p}")
     for i in range(3):                    # first K fragments of the next block (K(t+2) is visible)
-        issue_k(A, i)
+        issue_k(A, i, (u + 2) % NKBUF)
     A.e(f"Lnopre{p}:")
     A.e("s_waitcnt vmcnt(0)")
     A.e("s_barrier")
     A.e(f"s_add_u32 {sr(S_T)}, {sr(S_T)}, 1")
-    buf_index(A, S_B0, 1)
 
 
-def last(A, parity, uid):
-    cur, nxt = (V_SA, V_SB) if parity == 0 else (V_SB, V_SA)
-    A.e(f"Llast{parity}_{uid}:")
-    rotate(A, VA, 0)                      # va: buffer (t-1) mod 3 -> t mod 3 (no copies remain)
-    block(A, cur, nxt, False, False)
+def last(A, u, uid):
+    cur, nxt = (V_SA, V_SB) if u % 2 == 0 else (V_SB, V_SA)
+    A.e(f"Llast{u}_{uid}:")
+    block(A, cur, nxt, False, False, (u + 1) % NKBUF, u % NVBUF)
     A.e(f"s_branch Lend_{uid}")
 
 
@@ -497,7 +467,6 @@ def gen_loop():
     A = Asm()
     uid = "%="
     A.e(f"s_mov_b32 {sr(S_T)}, 0")
-    A.e(f"s_mov_b32 {sr(S_B0)}, 0")
     A.e(f"s_mov_b32 {sr(S_KP)}, %[kp_lo]")
     A.e(f"s_mov_b32 {sr(S_KP + 1)}, %[kp_hi]")
     A.e(f"s_mov_b32 {sr(S_VP)}, %[vp_lo]")
@@ -506,14 +475,14 @@ def gen_loop():
     A.e(f"s_cbranch_scc0 Lend_{uid}")
     A.e("s_cmp_lt_u32 1, %[nkt]")
     A.e(f"s_cbranch_scc0 Ltop_{uid}")
-    for i in range(3):                    # first K fragments of tile 1 (ka points at buffer 1)
-        issue_k(A, i)
+    for i in range(3):                    # first K fragments of tile 1 (K buffer 1)
+        issue_k(A, i, 1)
     A.e(f"Ltop_{uid}:")
-    half(A, 0, uid)
-    half(A, 1, uid)
+    for u in range(NKBUF):
+        half(A, u, uid)
     A.e(f"s_branch Ltop_{uid}")
-    last(A, 0, uid)
-    last(A, 1, uid)
+    for u in range(NKBUF):
+        last(A, u, uid)
     A.e(f"Lend_{uid}:")
     # the code after the statement reads O^T, written by the last value-product MFMAs: >= 24 wait
     # states (the compiler does not see the MFMAs inside the statement)
@@ -541,7 +510,7 @@ def main(out):
 # Registers the loop writes besides its own read-write operands (pinned sets and clobbers).
 WRITTEN = {"v": set(VCLOB) | set(range(V_SA, 256)), "s": set(SCLOB), "a": set(range(A_O, A_O + 128))}
 READ_WRITE_OPERANDS = tuple([f"mrun{q}" for q in range(2)] + [f"lrun{q}" for q in range(2)]
-                            + [f"nmc{q}" for q in range(2)] + KA + VA)
+                            + [f"nmc{q}" for q in range(2)])
 
 
 def _regs(tok):
@@ -560,7 +529,8 @@ def check_operand_allocation(compiled_asm: str) -> dict:
     {operand: register} of the last instance; raises AssertionError on a violation."""
     tpl = gen_loop()
     blocks = re.findall(r";;#ASMSTART\n(.*?);;#ASMEND", compiled_asm, flags=re.S)
-    loops = [b for b in blocks if [l.strip() for l in b.strip().splitlines()[:2]] == tpl[:2]]
+    loops = [b for b in blocks if b.strip().splitlines()[0].strip() == tpl[0]
+             and sum(1 for l in b.strip().splitlines() if l.strip()) == len(tpl)]
     assert loops, "loop statement not found in the compiled assembly"
     result = {}
     for body in loops:

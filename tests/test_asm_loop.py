@@ -69,12 +69,20 @@ def test_wide_generated_loop_is_current(tmp_path):
 
 def test_wide_loop_structure():
     lines = GW.gen_loop()
-    # 64 MFMAs per tile with a successor (two parities x unmasked/masked), 32 per last tile
-    assert sum(l.startswith("v_mfma") for l in lines) == 2 * 2 * 64 + 2 * 32
+    # 64 MFMAs per tile with a successor (four unrolled tiles x unmasked/masked), 32 per last tile
+    assert sum(l.startswith("v_mfma") for l in lines) == 4 * 2 * 64 + 4 * 32
     for l in lines:
         if "lgkmcnt(" in l:
             assert 0 <= int(l.split("lgkmcnt(")[1].rstrip(")")) <= 15
-    assert sum(l == "s_barrier" for l in lines) == 2
+    assert sum(l == "s_barrier" for l in lines) == 4
+    # every LDS read addresses a fixed buffer: an instruction offset inside the 4 K / 2 V buffers
+    for l in lines:
+        if l.startswith("ds_read"):
+            off = int(l.split("offset:")[1])
+            limit = 4 * 16384 if "%[ka" in l else 2 * 16384
+            assert 0 <= off < limit, l
+    # no per-tile address arithmetic on the read addresses
+    assert not any(l.startswith("v_add_u32") and "%[ka" in l or "%[va" in l and l.startswith("v_add") for l in lines)
     # tile copies are only ever waited for as a whole, before a barrier
     assert not any(l.startswith("s_waitcnt vmcnt(") and l != "s_waitcnt vmcnt(0)" for l in lines)
 
@@ -120,7 +128,7 @@ def test_lds_waits_cover_every_fragment_use(gen):
             A = mod.Asm()
             if gen == "wide":
                 cur, nxt = (GW.V_SA, GW.V_SB) if parity == 0 else (GW.V_SB, GW.V_SA)
-                GW.block(A, cur, nxt, has_next, masked)
+                GW.block(A, cur, nxt, has_next, masked, (parity + 1) % GW.NKBUF, parity % GW.NVBUF)
                 # entry state: K fragments 0..2 of the next tile in flight (issued before the barrier)
                 entry = [_regset(f"v[{GW.V_KF + 4 * i}:{GW.V_KF + 4 * i + 3}]") for i in range(3)] if has_next else []
             else:
