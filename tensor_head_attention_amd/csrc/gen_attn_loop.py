@@ -246,11 +246,10 @@ def block(A, cur_base, nxt_base, kbuf, vbuf, has_next, mask_next, extra_a=()):
     A.e(f"v_add_f32_e32 %[lrun], %[lrun], {vr(RS)}")
 
 
-def rescale(A, lbl):
-    """After phase B, when the test found a row whose tile max exceeds m_run + thr (SCC set; rare):
-    raise the running max of those rows, rescale O^T and l_run, and follow with neg_mc.  T0 holds
-    m_run + thr and MX the row max of tile t+1."""
-    A.e(f"s_cbranch_scc0 {lbl}")
+def rescale(A):
+    """Out-of-line path, taken after phase B when the test found a row whose tile max exceeds
+    m_run + thr (SCC set; rare): raise the running max of those rows, rescale O^T and l_run, and
+    follow with neg_mc.  T0 holds m_run + thr and MX the row max of tile t+1."""
     # O^T, written by the value product just before, is read by VALU below: >= 24 wait states
     A.e("s_nop 7")
     A.e("s_nop 7")
@@ -276,7 +275,6 @@ def rescale(A, lbl):
     A.e(f"v_cmp_eq_f32_e32 vcc, 0xff800000, %[mrun]")
     A.e(f"v_cndmask_b32_e64 %[nmc], %[nmc], 0, vcc")
     A.e("s_nop 1")
-    A.e(f"{lbl}:")
 
 
 def dma_groups(which, ahead, buf):
@@ -309,8 +307,10 @@ def dma_groups(which, ahead, buf):
     return g
 
 
-def half(A, parity, uid):
-    """Process tile t (= S_T) whose S lives in set A (parity 0) or B (parity 1)."""
+def half(A, parity, uid, cold):
+    """Process tile t (= S_T) whose S lives in set A (parity 0) or B (parity 1).  The common path
+    (an unmasked tile that moves no running max) runs straight through; the masked block and the
+    rescale go to `cold`, emitted after the loop, and branch back."""
     cur_base, nxt_base = (SA_BASE, SB_BASE) if parity == 0 else (SB_BASE, SA_BASE)
     kb_read = 1 - parity       # K buffer holding tile t+1
     vb_read = parity           # V buffer holding tile t
@@ -326,11 +326,15 @@ def half(A, parity, uid):
     A.e(f"s_cmp_ge_u32 {sr(S_T1)}, %[tmask]")
     A.e(f"s_cbranch_scc1 Lmask{p}")
     block(A, cur_base, nxt_base, kb_read, vb_read, True, False, extra_a)
-    A.e(f"s_branch Lpost{p}")
-    A.e(f"Lmask{p}:")
-    block(A, cur_base, nxt_base, kb_read, vb_read, True, True, extra_a)
     A.e(f"Lpost{p}:")
-    rescale(A, f"Lnorescale{p}")
+    A.e(f"s_cbranch_scc1 Lresc{p}")       # SCC from the rescale test: some row's max moved
+    A.e(f"Lback{p}:")
+    cold.e(f"Lmask{p}:")
+    block(cold, cur_base, nxt_base, kb_read, vb_read, True, True, extra_a)
+    cold.e(f"s_branch Lpost{p}")
+    cold.e(f"Lresc{p}:")
+    rescale(cold)
+    cold.e(f"s_branch Lback{p}")
     A.e("s_waitcnt vmcnt(0)")
     A.e("s_barrier")
     A.e(f"s_add_u32 {sr(S_T)}, {sr(S_T)}, 1")
@@ -355,11 +359,13 @@ def gen_loop():
     A.e(f"s_cmp_lt_u32 {sr(S_T)}, %[nkt]")
     A.e(f"s_cbranch_scc0 Lend_{uid}")
     A.e(f"Ltop_{uid}:")
-    half(A, 0, uid)
-    half(A, 1, uid)
+    cold = Asm()
+    half(A, 0, uid, cold)
+    half(A, 1, uid, cold)
     A.e(f"s_cmp_lt_u32 {sr(S_T)}, %[nkt]")
     A.e(f"s_cbranch_scc1 Ltop_{uid}")
     A.e(f"s_branch Lend_{uid}")
+    A.lines += cold.lines
     last(A, 0, uid)
     last(A, 1, uid)
     A.e(f"Lend_{uid}:")

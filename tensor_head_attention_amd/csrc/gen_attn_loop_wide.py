@@ -342,16 +342,14 @@ def block(A, cur, nxt, has_next, masked, kbuf, vbuf, extra_a=(), extra_b=()):
 
 
 def rescale_rows(A, p):
-    """After phase B: when the test of slot 29 found a row whose tile max exceeds its running max
-    by more than thr (rare), rescale the affected row blocks; otherwise fall through."""
-    A.e(f"s_cbranch_scc0 Lnoresc{p}")
+    """Out-of-line path, taken after phase B when the test of slot 29 found a row whose tile max
+    exceeds its running max by more than thr (rare): rescale the affected row blocks."""
     # O^T, written by the value product just before, is read by VALU below: >= 24 wait states
     A.e("s_nop 7")
     A.e("s_nop 7")
     A.e("s_nop 7")
     rescale(A, 0, f"Lnor0_{p}")
     rescale(A, 1, f"Lnor1_{p}")
-    A.e(f"Lnoresc{p}:")
 
 
 def rescale(A, qb, lbl):
@@ -425,8 +423,10 @@ KA = [f"ka{t}" for t in range(8)]
 VA = [f"va{d}" for d in range(4)]
 
 
-def half(A, u, uid):
-    """Tile t with t mod 4 == u (when t + 1 < nkt; else the last block)."""
+def half(A, u, uid, cold):
+    """Tile t with t mod 4 == u (when t + 1 < nkt; else the last block).  The common path (an
+    unmasked tile that moves no running max) runs straight through; the masked block and the
+    rescale go to `cold`, emitted after the loop, and branch back."""
     cur, nxt = (V_SA, V_SB) if u % 2 == 0 else (V_SB, V_SA)
     p = f"{u}_{uid}"
     # Scalar work of the tile, spread over the MFMA slots of phase A: K(t+3) -> K buffer (t+3) mod 4
@@ -440,11 +440,15 @@ def half(A, u, uid):
     A.e(f"s_cmp_ge_u32 {sr(S_T1)}, %[tmask]")
     A.e(f"s_cbranch_scc1 Lmask{p}")
     block(A, cur, nxt, True, False, (u + 1) % NKBUF, u % NVBUF, extra_a)
-    A.e(f"s_branch Lpost{p}")
-    A.e(f"Lmask{p}:")
-    block(A, cur, nxt, True, True, (u + 1) % NKBUF, u % NVBUF, extra_a)
     A.e(f"Lpost{p}:")
-    rescale_rows(A, p)
+    A.e(f"s_cbranch_scc1 Lresc{p}")       # SCC from the rescale test: some row's max moved
+    A.e(f"Lback{p}:")
+    cold.e(f"Lmask{p}:")
+    block(cold, cur, nxt, True, True, (u + 1) % NKBUF, u % NVBUF, extra_a)
+    cold.e(f"s_branch Lpost{p}")
+    cold.e(f"Lresc{p}:")
+    rescale_rows(cold, p)
+    cold.e(f"s_branch Lback{p}")
     A.e(f"s_add_u32 {sr(S_TMP)}, {sr(S_T)}, 2")
     A.e(f"s_cmp_lt_u32 {sr(S_TMP)}, %[nkt]")
     A.e(f"s_cbranch_scc0 Lnopre{p}")
@@ -478,9 +482,11 @@ def gen_loop():
     for i in range(3):                    # first K fragments of tile 1 (K buffer 1)
         issue_k(A, i, 1)
     A.e(f"Ltop_{uid}:")
+    cold = Asm()
     for u in range(NKBUF):
-        half(A, u, uid)
+        half(A, u, uid, cold)
     A.e(f"s_branch Ltop_{uid}")
+    A.lines += cold.lines
     for u in range(NKBUF):
         last(A, u, uid)
     A.e(f"Lend_{uid}:")
