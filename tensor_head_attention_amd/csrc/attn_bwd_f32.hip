@@ -34,7 +34,42 @@ __device__ __forceinline__ float ld(const T* p, int64_t i) {
   return (float)p[i];
 }
 
-// Delta_i = dout_i . o_i for every (b, h, i), into delta [B, H, Sq]: one wavefront per row.
+// Delta_i = dout_i . o_i for every (b, h, i), into delta [B, H, Sq]; vector form.  A row of D
+// elements is `lanes` = D / (16-byte vector) consecutive threads, rows taken in memory order
+// ([B, Sq, H] rows of o and dout are contiguous), so both inputs stream as whole lines; blocks are
+// spread so that each XCD takes a contiguous share of the tokens, and the 4-byte delta writes of
+// neighbouring tokens (adjacent in [B, H, Sq]) stay in one XCD's L2.  HBM-bound: 2 * D * elem
+// bytes read and 4 written per row.
+template <typename T>
+__global__ void __launch_bounds__(256) bwd_delta_vec_kernel(const T* __restrict__ o, const T* __restrict__ dout,
+                                                           float* __restrict__ delta, int64_t rows, int Sq, int H,
+                                                           int D, int lanes_log2) {
+  constexpr int kE = 16 / (int)sizeof(T);
+  const int lanes = 1 << lanes_log2;
+  const int lir = threadIdx.x & (lanes - 1);
+  const int64_t r = (int64_t)xcd_contiguous_block(blockIdx.x, gridDim.x) * (256 >> lanes_log2) +
+                    (threadIdx.x >> lanes_log2);  // (b*Sq + i)*H + h
+  float acc = 0.f;
+  if (r < rows) {
+    const int64_t off = r * D + (int64_t)lir * kE;
+    const i32x4 x = __builtin_nontemporal_load((const i32x4*)(o + off));
+    const i32x4 y = __builtin_nontemporal_load((const i32x4*)(dout + off));
+    const T* xv = (const T*)&x;
+    const T* yv = (const T*)&y;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) acc = fmaf((float)xv[e], (float)yv[e], acc);
+  }
+  for (int m = lanes >> 1; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 64);  // within the row's lanes
+  if (r < rows && lir == 0) {
+    const int64_t bi = r / H;
+    const int h = (int)(r - bi * H);
+    const int64_t b = bi / Sq;
+    const int i = (int)(bi - b * Sq);
+    delta[(b * H + h) * Sq + i] = acc;
+  }
+}
+
+// Delta for any D and alignment: one wavefront per row.
 template <typename T>
 __global__ void __launch_bounds__(kWaves * 64) bwd_delta_kernel(const T* __restrict__ o, const T* __restrict__ dout,
                                                                 float* __restrict__ delta, int B, int Sq, int H, int D) {
@@ -210,6 +245,26 @@ __global__ void __launch_bounds__(kWaves * 64) bwd_dkdv_f32_kernel(
 
 hipError_t launch_attn_bwd_delta(const AttnBwdArgs& a, int in_dt, hipStream_t st) {
   const int64_t rows = (int64_t)a.B * a.H * a.Sq;
+  {
+    const int ke = in_dt == THA_F32 ? 4 : 8;  // elements per 16-byte vector
+    const int lanes = a.D / ke;
+    const bool vec = a.D % ke == 0 && lanes >= 1 && lanes <= 64 && (lanes & (lanes - 1)) == 0 &&
+                     (uintptr_t)a.o % 16 == 0 && (uintptr_t)a.dout % 16 == 0;
+    if (vec) {
+      int ll = 0;
+      while ((1 << ll) < lanes) ++ll;
+      const int64_t rpb = 256 >> ll;
+      const int64_t vblocks = (rows + rpb - 1) / rpb;
+      if (vblocks > 0x7fffffff) return hipErrorInvalidValue;
+      if (in_dt == THA_F32)
+        hipLaunchKernelGGL(bwd_delta_vec_kernel<float>, dim3((unsigned)vblocks), dim3(256), 0, st, (const float*)a.o,
+                           (const float*)a.dout, a.delta, rows, a.Sq, a.H, a.D, ll);
+      else
+        hipLaunchKernelGGL(bwd_delta_vec_kernel<__bf16>, dim3((unsigned)vblocks), dim3(256), 0, st,
+                           (const __bf16*)a.o, (const __bf16*)a.dout, a.delta, rows, a.Sq, a.H, a.D, ll);
+      return hipGetLastError();
+    }
+  }
   const int64_t blocks = (rows + kWaves - 1) / kWaves;
   if (blocks > 0x7fffffff || a.D > 1024) return hipErrorInvalidValue;
   if (in_dt == THA_F32)
