@@ -326,17 +326,24 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dkdv_kernel(KArgs a) {
   cp.init(wave, lane, (uint32_t)(rs * 2));
   const __bf16* qbase = a.q + (int64_t)b * a.Sq * rs + (int64_t)h * D;
   const __bf16* dbase = a.dout + (int64_t)b * a.Sq * rs + (int64_t)h * D;
-  auto stats = [&](int t, int slot) {  // lse and Delta of the 32 rows of query tile t
+  // lse and Delta of the 32 rows of query tile t: loaded by the first 32 lanes (load_stats) and
+  // stored to LDS after the tile's products (store_stats), so the loads' latency is hidden
+  float st_l = -INFINITY, st_d = 0.f;
+  auto load_stats = [&](int t) {
     if (tid < kTq) {
       const int r = t * kTq + tid;
-      float L = INFINITY, Dv = 0.f;
+      st_l = -INFINITY;
+      st_d = 0.f;
       if (r < a.Sq) {
-        const float l = a.lse[(int64_t)bh * a.Sq + r];
-        L = l == -INFINITY ? INFINITY : l * kLog2e;
-        Dv = a.delta[(int64_t)bh * a.Sq + r];
+        st_l = a.lse[(int64_t)bh * a.Sq + r];
+        st_d = a.delta[(int64_t)bh * a.Sq + r];
       }
-      lt[slot][tid] = L;
-      dt[slot][tid] = Dv;
+    }
+  };
+  auto store_stats = [&](int slot) {
+    if (tid < kTq) {
+      lt[slot][tid] = st_l == -INFINITY ? INFINITY : st_l * kLog2e;
+      dt[slot][tid] = st_d;
     }
   };
 
@@ -349,7 +356,8 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dkdv_kernel(KArgs a) {
   if (qt0 < n_qt) {
     cp.copy(qbase, rs, qt0 * kTq, a.Sq, qbuf, wave);
     cp.copy(dbase, rs, qt0 * kTq, a.Sq, dbuf, wave);
-    stats(qt0, 0);
+    load_stats(qt0);
+    store_stats(0);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -358,7 +366,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dkdv_kernel(KArgs a) {
     if (t + 1 < n_qt) {
       cp.copy(qbase, rs, (t + 1) * kTq, a.Sq, qbuf + (buf ^ 1) * kTileBytes, wave);
       cp.copy(dbase, rs, (t + 1) * kTq, a.Sq, dbuf + (buf ^ 1) * kTileBytes, wave);
-      stats(t + 1, buf ^ 1);
+      load_stats(t + 1);
     }
     const int qt0_row = t * kTq;
     bool skip = k0 >= kv_lim;
@@ -414,6 +422,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dkdv_kernel(KArgs a) {
         }
       }
     }
+    if (t + 1 < n_qt) store_stats(buf ^ 1);  // the other slot: read by no wave in this tile
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
