@@ -180,11 +180,15 @@ THA_API int attn_bwd(const void* q, const void* k, const void* v, const void* o,
  *
  *   o_parts   host array of n_parts device pointers, each [B, S, H, D] of part_dt
  *   lse_parts host array of n_parts device pointers, each [B, H, S] float32
- *   o_out     [B, S, H, D] of out_dt; may alias o_parts[0] when part_dt == out_dt
- *   lse_out   [B, H, S] float32 or NULL; may alias lse_parts[0]
+ *   o_out     [B, S, H, D] of out_dt; may be any o_parts[k] when part_dt == out_dt
+ *             (in place: each element is written by the thread that read it
+ *             from every part)
+ *   lse_out   [B, H, S] float32 or NULL; may be any lse_parts[k] (a row's lse
+ *             values are all read before its one lse store)
+ * Partial overlaps between o_out and a part are not allowed.
  * 1 <= n_parts <= THA_MAX_PARTS; part_dt, out_dt in {THA_F32, THA_BF16}.
  * Errors: THA_ERR_INVALID for null pointers, n_parts out of range,
- * non-positive sizes, or o_out aliasing o_parts[0] with differing dtypes;
+ * non-positive sizes, or o_out equal to an o_parts[k] with differing dtypes;
  * THA_ERR_UNSUPPORTED for other dtypes.
  */
 THA_API int attn_merge_lse(int n_parts, const void* const* o_parts, const float* const* lse_parts, int part_dt,

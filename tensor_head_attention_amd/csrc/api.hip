@@ -158,7 +158,8 @@ int attn_merge_lse(int n_parts, const void* const* o_parts, const float* const* 
     pp.lse[i] = lse_parts[i];
   }
   if (!dtype_ok(part_dt) || !dtype_ok(out_dt)) return THA_ERR_UNSUPPORTED;
-  if (o_out == o_parts[0] && part_dt != out_dt) return THA_ERR_INVALID;
+  for (int i = 0; i < n_parts && part_dt != out_dt; ++i)  // in place needs equal element sizes
+    if (o_out == o_parts[i]) return THA_ERR_INVALID;
   return hip_status(
       tha::launch_merge_lse(n_parts, pp, part_dt, o_out, out_dt, lse_out, B, S, H, D, (hipStream_t)stream));
 }

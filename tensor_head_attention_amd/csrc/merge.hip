@@ -61,8 +61,8 @@ __device__ __forceinline__ void store1(void* p, int64_t i, float v) {
 // of two, <= 256).  The data loads of the first 8 parts are issued before the lse reads, so a
 // workgroup waits for memory once rather than twice (lse, then data).  Every thread reads the row's
 // lse values before the block barrier and the row's single lse store comes after it, so lse_out may
-// alias lse_parts[0]; each output element is written by the thread that read it, so o_out may alias
-// o_parts[0].
+// be any lse_parts[k]; each output element is written by the thread that read it from every part, so
+// o_out may be any o_parts[k] of the same element type.
 template <typename PartT, typename OutT>
 __global__ void __launch_bounds__(kThreads) merge_vec_kernel(PartPtrs parts, int n, void* o_out, float* lse_out,
                                                             int64_t rows, int S, int H, int D, int lanes_log2) {

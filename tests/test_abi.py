@@ -160,6 +160,7 @@ def test_merge_validation(lib):
     assert call(pdt=3) == U
     assert call(odt=3) == U
     assert call(o=_ptr_arr(2, 0x2000), out=ctypes.c_void_p(0x2000), pdt=0, odt=1) == E  # in place, dtypes differ
+    assert call(o=(ctypes.c_void_p * 2)(0x1000, 0x2000), out=ctypes.c_void_p(0x2000), pdt=1, odt=0) == E  # part 1
 
 
 def test_permute_validation(lib):

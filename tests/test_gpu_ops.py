@@ -108,3 +108,19 @@ def test_merge_in_place_streaming():
     torch.cuda.synchronize()
     check_out(o_run, ref, torch.float32)
     check_lse(l_run, ref_lse, torch.float32)
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("D", [128, 22])  # the vector and the scalar kernel
+def test_merge_in_place_any_part(dt, D):
+    """o_out and lse_out may be any part (here the last of three), not only the first."""
+    n, B, S, H = 3, 2, 70, 4
+    os_, ls_ = _parts(n, B, S, H, D, seed=78, part_dtype=dt)
+    ref, ref_lse = oracle.merge_lse([o.double() for o in os_], [l.double() for l in ls_])
+    od, ld = to_dev(*os_), to_dev(*ls_)
+    expect, expect_lse = T.attn_merge_lse(od, ld, out_dtype=dt)
+    T.attn_merge_lse(od, ld, out=od[-1], lse_out=ld[-1])
+    torch.cuda.synchronize()
+    assert torch.equal(od[-1], expect) and torch.equal(ld[-1], expect_lse)
+    check_out(od[-1], ref, dt)
+    check_lse(ld[-1], ref_lse, torch.float32)
