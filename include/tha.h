@@ -83,7 +83,8 @@ enum {
  * mask_flags: THA_MASK_CAUSAL and/or THA_MASK_KEY_PADDING.  q_pos0 / k_pos0 are
  * the global sequence positions of query row 0 and key 0 (global position ids,
  * as in the data collator of "Support deepspeed sequence parallel"); they only
- * matter with THA_MASK_CAUSAL.  kv_len: device int32 [B], required iff
+ * matter with THA_MASK_CAUSAL, and only through q_pos0 - k_pos0 (any values
+ * with |q_pos0|, |k_pos0| < 2^62 are exact).  kv_len: device int32 [B], required iff
  * THA_MASK_KEY_PADDING (values are clamped to [0, Sk] on the device).
  * scale: multiplies q.k, finite and > 0; pass 1/sqrt(D) for standard attention.
  *

@@ -15,6 +15,16 @@ constexpr int64_t kMaxRowElems = 1LL << 24;  // H*D per token: tile offsets stay
 
 int hip_status(hipError_t e) { return e == hipSuccess ? THA_OK : THA_ERR_HIP; }
 
+// Causal visibility depends on the positions only through their difference: key j is visible to
+// query row i iff j - i <= q_pos0 - k_pos0.  The kernels receive that difference as q_pos0 (with
+// k_pos0 = 0), clamped to +-2^40, far beyond any row or key index (< 2^31), so the visible sets
+// are unchanged and the kernels' 64-bit index sums (position + index) cannot overflow.
+constexpr long long kPosDiffClamp = 1LL << 40;
+long long pos_diff(long long q_pos0, long long k_pos0) {  // |q_pos0|, |k_pos0| < 2^62: no overflow
+  const long long d = q_pos0 - k_pos0;
+  return d > kPosDiffClamp ? kPosDiffClamp : (d < -kPosDiffClamp ? -kPosDiffClamp : d);
+}
+
 bool dtype_ok(int dt) { return dt == THA_F32 || dt == THA_BF16; }
 
 int check_permute(const void* grouped, const void* const* shards, int P, int group, int B, int S, int H, int D,
@@ -87,7 +97,7 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, int out_dt,
   a.B = B, a.Sq = Sq, a.Sk = Sk, a.H = H, a.D = D;
   a.out_dt = out_dt;
   a.causal = (flags & THA_MASK_CAUSAL) != 0;
-  a.q_pos0 = q_pos0, a.k_pos0 = k_pos0;
+  a.q_pos0 = pos_diff(q_pos0, k_pos0), a.k_pos0 = 0;
   a.scale = scale;
   a.q_bs = st8[0], a.q_rs = st8[1], a.k_bs = st8[2], a.k_rs = st8[3];
   a.v_bs = st8[4], a.v_rs = st8[5], a.o_bs = st8[6], a.o_rs = st8[7];
@@ -138,7 +148,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   a.kv_len = (mask_flags & THA_MASK_KEY_PADDING) ? kv_len : nullptr;
   a.B = B, a.Sq = Sq, a.Sk = Sk, a.H = H, a.D = D;
   a.causal = (mask_flags & THA_MASK_CAUSAL) != 0;
-  a.q_pos0 = q_pos0, a.k_pos0 = k_pos0;
+  a.q_pos0 = pos_diff(q_pos0, k_pos0), a.k_pos0 = 0;
   a.scale = scale;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = tha::launch_attn_bwd_delta(a, in_dt, st);
