@@ -425,14 +425,35 @@ def cpu_baseline(grouped, S, H, D, n_rows):
     # rows spread evenly over the sequence (later rows see more keys)
     rows = torch.linspace(0, S - 1, n_rows).round().to(torch.int64)
     pairs = int(sum(int(r) + 1 for r in rows)) * H
-    cores = os.cpu_count() or 1
+    cores = cpu_share()
     t0 = time.perf_counter()
     oracle.attention(q, k, v, causal=True, rows=rows, nthreads=cores)
     dt = time.perf_counter() - t0
+    # per-core rate: one thread on every cores-th row of the same sample (about the same seconds)
+    rows1 = rows[::cores]
+    pairs1 = int(sum(int(r) + 1 for r in rows1)) * H
+    t0 = time.perf_counter()
+    oracle.attention(q, k, v, causal=True, rows=rows1, nthreads=1)
+    dt1 = time.perf_counter() - t0
     return {"value": 4.0 * D * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": min(cores, n_rows), "kind": "oracle",
             "seconds": round(dt, 3),
             "sample": f"{n_rows} query rows evenly spaced over S={S} (all {H} heads, causal prefixes), "
-                      f"{pairs} visible pairs; fp64 two-pass oracle on {cores} host threads ({cpu_model()})"}
+                      f"{pairs} visible pairs; fp64 two-pass oracle on {cores} host threads ({cpu_model()})",
+            "per_core_value": 4.0 * D * pairs1 / dt1 / 1e12,
+            "per_core_sample": f"{len(rows1)} of those rows ({pairs1} pairs) on one thread, {dt1:.3f} s"}
+
+
+def cpu_share() -> int:
+    """Host threads for the oracle: the CPUs this process may run on, capped by OMP_NUM_THREADS
+    when that is set (the CPU share a machine gives one GPU's job)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
 
 
 if __name__ == "__main__":
