@@ -76,7 +76,8 @@ def attn_traffic():
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
+    # 120 timed steps: about 0.23 s of timed work (at least 30 repetitions and 200 ms)
+    ap.add_argument("--steps", type=int, default=120)
     # The first ~20 calls of a run are a transient (clocks and power management settling: the kernel
     # trace shows the attention falling from ~2.2 to ~1.8 ms over them); 25 warm-up steps put the
     # timed steps in steady state.
