@@ -94,3 +94,22 @@ def test_rescale_narrow_wide_bitwise(recipe):
     ref, ref_lse = oracle.attention(q, k, v, causal=True, q_pos0=1000)
     check_out(res["wide"][0], ref, torch.bfloat16)
     check_lse(res["wide"][1], ref_lse, torch.bfloat16)
+
+
+@pytest.mark.parametrize("recipe", ["spikes", "rising"])
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "partials"])
+def test_ring_share_large_jumps(recipe, fused):
+    """A Ring pass over chunks whose scores differ by tens of units between chunks: the merge of
+    running results (in the attention epilogue, or by attn_merge_lse) meets weights e^(lse_k - M)
+    far from 1 in both directions."""
+    say(f"ring share {recipe} fused={fused}")
+    q, k, v = inputs(recipe, 1, 256, 1100, 2, 128, torch.bfloat16, seed=913)
+    ref, ref_lse = oracle.attention(q, k, v, causal=True, q_pos0=844)
+    qd, kd, vd = to_dev(q, k, v)
+    cuts = [0, 200, 421, 700, 1030, 1100]
+    kc = [kd[:, a:b].contiguous() for a, b in zip(cuts, cuts[1:])]
+    vc = [vd[:, a:b].contiguous() for a, b in zip(cuts, cuts[1:])]
+    out, lse = T.ring_share(qd, kc, vc, q_pos0=844, k_pos0s=cuts[:-1], fused=fused, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_out(out, ref, torch.bfloat16)
+    check_lse(lse, ref_lse, torch.bfloat16)
