@@ -25,6 +25,8 @@ def _bits(t):
     (1, 1, 5, 2, 16, torch.bfloat16),     # P = 1 is a plain copy
     (2, 2, 14, 4, 32, torch.bfloat16),    # odd shard length (7 tokens): plain visiting order
     (3, 2, 18, 6, 24, torch.bfloat16),    # 96-byte runs (6 vectors, not a power of two), even/odd order
+    (16, 2, 64, 32, 16, torch.float32),   # 16 shards
+    (64, 1, 128, 64, 8, torch.bfloat16),  # the most shards a call takes; 16-byte runs, 2 tokens a shard
 ])
 def test_permute_and_unpermute_bit_exact(P, B, S, H, D, dtype):
     say(f"permute P{P} B{B} S{S} H{H} D{D} {dtype}")
