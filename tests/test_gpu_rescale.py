@@ -3,9 +3,9 @@ row's running max is set by its first key tile and almost never raised again, so
 and l (taken when a tile's maximum exceeds the running max by more than 2^8 in probability terms)
 would only ever act on zeros.  Two recipes add a common direction u (|u| = 1) to every query and,
 with a weight per key, to the keys:
-  spikes: a few keys get weights that put their scores about 6-12 above the bulk of the row (how far
-          depends on the row's q.u), so the running max is raised mid-row while the keys before the
-          spike still hold a large share of the softmax mass, and a wrong rescale of O or l shows;
+  spikes: four keys get weights that put their scores about 8, 11, 15 and 19 times the row's q.u
+          (about 1) above the bulk of the row, so the running max is raised mid-row while the keys
+          before a spike still hold a large share of the softmax mass, and a wrong rescale shows;
   rising: the weight grows along the sequence, so the scores of a row rise by several units per key
           tile and the running max is raised again and again."""
 import pytest
