@@ -44,6 +44,8 @@ CASES = [
     (2, 129, 257, 2, 64, torch.bfloat16, False, 0, 0, [200, 257]),
     (1, 1, 1, 1, 128, torch.bfloat16, False, 0, 0, None),
     (1, 1, 700, 1, 128, torch.bfloat16, True, 699, 0, None),        # decode-like single row
+    (48, 70, 70, 1, 128, torch.bfloat16, True, 0, 0, None),         # many sequences, one head
+    (5, 90, 130, 40, 128, torch.bfloat16, False, 0, 0, [130, 1, 64, 0, 99]),  # 40 heads: 10 KiB tokens
     (1, 64, 64, 2, 8, torch.float32, True, 0, 0, None),
     (2, 70, 90, 3, 40, torch.float32, False, 0, 0, [90, 17]),
     (1, 33, 200, 2, 256, torch.float32, True, 167, 0, None),
