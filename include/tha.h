@@ -61,7 +61,14 @@ enum {
   THA_MASK_CAUSAL = 1,     /* key visible iff k_pos0 + j <= q_pos0 + i ("adv07: Sequence Parallel", Q4) */
   THA_MASK_KEY_PADDING = 2, /* key j of sequence b visible iff j < kv_len[b] ("Support deepspeed
                                sequence parallel": the mask is 'token is not padding') */
-  THA_ACCUMULATE = 4         /* attn_fwd_ex only: merge into the running (o, lse), see there */
+  THA_ACCUMULATE = 4,        /* attn_fwd_ex only: merge into the running (o, lse), see there */
+  /* attn_fwd_ex only: force the kernel of the bf16, head-size-128 path (see attn_fwd); a 3-bit
+     field, 0 = automatic choice.  Ignored for other dtypes and head sizes. */
+  THA_KERNEL_AUTO = 0,
+  THA_KERNEL_NARROW = 1 << 3,
+  THA_KERNEL_WIDE = 2 << 3,
+  THA_KERNEL_SPLIT = 3 << 3,
+  THA_KERNEL_MASK = 7 << 3
 };
 
 /* Largest pointer arrays accepted by attn_merge_lse and the permutes. */
@@ -100,8 +107,12 @@ enum {
  * (two wavefront groups per workgroup on the two halves of the key range, merged by
  * log-sum-exp before the output is written).  All three compute the same function;
  * the wide and narrow kernels give identical bits, the split form differs from them
- * only by the association of the two key halves.  The environment variable
- * THA_ATTN_D128_KERNEL=narrow|wide|split, read on every call, forces one of them.
+ * only by the association of the two key halves (within the stated tolerances).
+ * The automatic choice depends on B*H, Sq and the device's compute-unit count, so the
+ * same rows computed by calls of different sizes (a query split, a Ring chunk against
+ * the whole call) may differ in the last bits when the calls take different forms;
+ * calls that take the same form give the same bits for the same rows.  attn_fwd_ex's
+ * THA_KERNEL_* flags force one form for every size.
  * Errors: THA_ERR_INVALID for null q/k/v/o, non-positive sizes, unknown mask
  * bits, KEY_PADDING without kv_len, scale not finite and positive, |q_pos0| or |k_pos0| >=
  * 2^62; THA_ERR_UNSUPPORTED for other dtypes / head dims.
@@ -125,7 +136,10 @@ THA_API int attn_fwd(const void* q, const void* k, const void* v, void* o, int o
  *   16-byte aligned with strides multiples of 8 elements, o 8-byte (bf16) or 16-byte (fp32)
  *   aligned with strides multiples of 4 elements (THA_ERR_UNSUPPORTED otherwise).
  *
- * flags: the mask flags of attn_fwd, plus THA_ACCUMULATE.  With THA_ACCUMULATE, o (out_dt must
+ * flags: the mask flags of attn_fwd, plus THA_ACCUMULATE and a THA_KERNEL_* value (bf16, D = 128
+ *   only: THA_KERNEL_NARROW, _WIDE or _SPLIT forces that form of the kernel instead of the
+ *   automatic choice described at attn_fwd, e.g. to get bit-identical rows from calls of different
+ *   sizes).  With THA_ACCUMULATE, o (out_dt must
  *   be THA_F32) and lse (required) hold a running result over other keys, and this call merges
  *   its own result into them in place by the log-sum-exp rule of attn_merge_lse (the Ring step
  *   that accumulates block results into the full attention, "adv07: Sequence Parallel" Q5),
@@ -164,7 +178,8 @@ THA_API int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, in
  * products that consume them); in_dt = THA_F32 with 1 <= D <= 256 (fp32
  * throughout).
  * Errors: as attn_fwd, plus THA_ERR_INVALID for a null o, dout, lse, dq, dk, dv
- * or workspace.
+ * or workspace; on the bf16 path THA_ERR_UNSUPPORTED when q, k, v, dout, dq, dk or dv
+ * is not 16-byte aligned (the kernels move 16-byte vectors).
  */
 THA_API int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
              float* dq, float* dk, float* dv, float* workspace, int B, int Sq, int Sk, int H, int D, int in_dt,

@@ -21,7 +21,10 @@ THA_OK, THA_ERR_INVALID, THA_ERR_UNSUPPORTED, THA_ERR_HIP = 0, -1, -2, -3
 THA_F32, THA_BF16 = 0, 1
 THA_MASK_NONE, THA_MASK_CAUSAL, THA_MASK_KEY_PADDING = 0, 1, 2
 THA_ACCUMULATE = 4
+THA_KERNEL_AUTO, THA_KERNEL_NARROW, THA_KERNEL_WIDE, THA_KERNEL_SPLIT = 0, 1 << 3, 2 << 3, 3 << 3
 THA_MAX_PARTS = THA_MAX_SHARDS = 64
+_KERNELS = {None: THA_KERNEL_AUTO, "auto": THA_KERNEL_AUTO, "narrow": THA_KERNEL_NARROW,
+            "wide": THA_KERNEL_WIDE, "split": THA_KERNEL_SPLIT}
 
 _lib = None
 
@@ -85,12 +88,52 @@ def _dt(t: torch.dtype) -> int:
     raise NotImplementedError(f"unsupported dtype {t}")
 
 
+def _is_device(t: torch.Tensor) -> bool:
+    return t.is_cuda
+
+
 def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
-    if not t.is_cuda:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not _is_device(t):
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
+
+
+# The C ABI sees raw pointers only, so every tensor's shape, dtype and device is checked here,
+# before any library call: a mismatch would otherwise read or write outside its buffer.
+def _expect(t: torch.Tensor, name: str, shape, dtype=None, device=None, dtypes=None):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t
+
+
+def _bshd(t: torch.Tensor, name: str):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D [B, S, H, D], got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
+def _kv_len_arg(kv_len, B: int, device):
+    if kv_len is None:
+        return 0, None
+    kv_len = _dev(kv_len, "kv_len")
+    _expect(kv_len, "kv_len", (B,), torch.int32, device)
+    return THA_MASK_KEY_PADDING, kv_len.data_ptr()
+
+
+def _kernel_flag(kernel) -> int:
+    if kernel not in _KERNELS:
+        raise ValueError(f"kernel must be one of {sorted(k for k in _KERNELS if k)} or None, got {kernel!r}")
+    return _KERNELS[kernel]
 
 
 def _stream(t: torch.Tensor) -> int:
@@ -105,37 +148,46 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool 
              kv_len: Optional[torch.Tensor] = None, q_pos0: int = 0, k_pos0: int = 0,
              scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-             return_lse: bool = True):
-    """out [B,Sq,H,D], lse [B,H,Sq] (fp32) = attention of q against k/v (see tha.h attn_fwd)."""
+             return_lse: bool = True, kernel: Optional[str] = None):
+    """out [B,Sq,H,D], lse [B,H,Sq] (fp32) = attention of q against k/v (see tha.h attn_fwd).
+    kernel: None (automatic) or "narrow" / "wide" / "split" to force the form of the bf16
+    head-size-128 kernel (attn_fwd_ex's THA_KERNEL_* flags)."""
     load_library()
     q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")
-    B, Sq, H, D = q.shape
-    Sk = k.shape[1]
+    B, Sq, H, D = _bshd(q, "q")
+    Sk = _bshd(k, "k")[1]
+    _expect(k, "k", (B, Sk, H, D), q.dtype, q.device)
+    _expect(v, "v", (B, Sk, H, D), q.dtype, q.device)
     if out is None:
         out = torch.empty((B, Sq, H, D), dtype=out_dtype or q.dtype, device=q.device)
-    _dev(out, "out")
+    _expect(_dev(out, "out"), "out", (B, Sq, H, D), None, q.device, (torch.bfloat16, torch.float32))
     if lse is None and return_lse:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
-    flags = THA_MASK_CAUSAL if causal else 0
-    kvp = None
-    if kv_len is not None:
-        kv_len = _dev(kv_len, "kv_len")
-        if kv_len.dtype != torch.int32:
-            raise ValueError("kv_len must be int32")
-        flags |= THA_MASK_KEY_PADDING
-        kvp = kv_len.data_ptr()
+    if lse is not None:
+        _expect(_dev(lse, "lse"), "lse", (B, H, Sq), torch.float32, q.device)
+    kflag, kvp = _kv_len_arg(kv_len, B, q.device)
+    flags = (THA_MASK_CAUSAL if causal else 0) | kflag
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    rc = _lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dt(out.dtype),
-                       lse.data_ptr() if lse is not None else None, B, Sq, Sk, H, D, _dt(q.dtype), flags,
-                       int(q_pos0), int(k_pos0), kvp, float(scale), _stream(q))
+    kf = _kernel_flag(kernel)
+    lp = lse.data_ptr() if lse is not None else None
+    if kf == THA_KERNEL_AUTO:
+        rc = _lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dt(out.dtype), lp,
+                           B, Sq, Sk, H, D, _dt(q.dtype), flags, int(q_pos0), int(k_pos0), kvp, float(scale),
+                           _stream(q))
+    else:
+        rc = _lib.attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dt(out.dtype), lp,
+                              B, Sq, Sk, H, D, _dt(q.dtype), flags | kf, int(q_pos0), int(k_pos0), kvp,
+                              float(scale), None, _stream(q))
     _check(rc, "attn_fwd")
     return (out, lse) if return_lse else out
 
 
 def _view_strides(t: torch.Tensor, name: str):
     """(batch, token) element strides of a [B, S, H, D] view with heads and dims contiguous."""
-    if not t.is_cuda:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not _is_device(t):
         raise ValueError(f"{name} must be a device tensor")
     if t.dim() != 4 or t.stride(3) != 1 or t.stride(2) != t.shape[3]:
         raise ValueError(f"{name} must be a [B, S, H, D] view with contiguous heads and dims")
@@ -146,14 +198,19 @@ def attn_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bo
                 kv_len: Optional[torch.Tensor] = None, q_pos0: int = 0, k_pos0: int = 0,
                 scale: Optional[float] = None, out_dtype: Optional[torch.dtype] = None,
                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                accumulate: bool = False):
+                accumulate: bool = False, kernel: Optional[str] = None):
     """attn_fwd on strided views (e.g. packed QKV [B,S,3,H,D] split into q, k, v; head subsets),
     and with accumulate=True the fused Ring step: out (fp32) and lse hold a running result over
     other keys and this call merges its own result into them (see tha.h attn_fwd_ex).
-    Returns (out, lse)."""
+    kernel: as attn_fwd.  Returns (out, lse)."""
     load_library()
+    strides = list(_view_strides(q, "q"))
     B, Sq, H, D = q.shape
+    strides += _view_strides(k, "k")
     Sk = k.shape[1]
+    _expect(k, "k", (B, Sk, H, D), q.dtype, q.device)
+    strides += _view_strides(v, "v")
+    _expect(v, "v", (B, Sk, H, D), q.dtype, q.device)
     if out is None:
         if accumulate:
             raise ValueError("accumulate needs the running out and lse")
@@ -162,19 +219,13 @@ def attn_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bo
         if accumulate:
             raise ValueError("accumulate needs the running out and lse")
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device)
-    _dev(lse, "lse")
-    strides = []
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
-        strides += list(_view_strides(t, n))
+    strides += _view_strides(out, "out")
+    _expect(out, "out", (B, Sq, H, D), None, q.device, (torch.bfloat16, torch.float32))
+    _expect(_dev(lse, "lse"), "lse", (B, H, Sq), torch.float32, q.device)
     st = (ctypes.c_longlong * 8)(*strides)
-    flags = (THA_MASK_CAUSAL if causal else 0) | (THA_ACCUMULATE if accumulate else 0)
-    kvp = None
-    if kv_len is not None:
-        kv_len = _dev(kv_len, "kv_len")
-        if kv_len.dtype != torch.int32:
-            raise ValueError("kv_len must be int32")
-        flags |= THA_MASK_KEY_PADDING
-        kvp = kv_len.data_ptr()
+    kflag, kvp = _kv_len_arg(kv_len, B, q.device)
+    flags = (THA_MASK_CAUSAL if causal else 0) | (THA_ACCUMULATE if accumulate else 0) | kflag
+    flags |= _kernel_flag(kernel)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     rc = _lib.attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _dt(out.dtype), lse.data_ptr(),
@@ -194,33 +245,29 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     load_library()
     q, k, v, o, dout, lse = (_dev(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"),
                                                         (lse, "lse")))
-    B, Sq, H, D = q.shape
-    Sk = k.shape[1]
-    if lse.dtype != torch.float32:
-        raise ValueError("lse must be float32")
+    B, Sq, H, D = _bshd(q, "q")
+    Sk = _bshd(k, "k")[1]
+    dev = q.device
+    _expect(k, "k", (B, Sk, H, D), q.dtype, dev)
+    _expect(v, "v", (B, Sk, H, D), q.dtype, dev)
+    _expect(o, "o", (B, Sq, H, D), q.dtype, dev)
+    _expect(dout, "dout", (B, Sq, H, D), q.dtype, dev)
+    _expect(lse, "lse", (B, H, Sq), torch.float32, dev)
     if dq is None:
-        dq = torch.zeros((B, Sq, H, D), dtype=torch.float32, device=q.device)
+        dq = torch.zeros((B, Sq, H, D), dtype=torch.float32, device=dev)
     if dk is None:
-        dk = torch.zeros((B, Sk, H, D), dtype=torch.float32, device=q.device)
+        dk = torch.zeros((B, Sk, H, D), dtype=torch.float32, device=dev)
     if dv is None:
-        dv = torch.zeros((B, Sk, H, D), dtype=torch.float32, device=q.device)
-    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
-        _dev(t, n)
-        if t.dtype != torch.float32:
-            raise ValueError(f"{n} must be float32")
+        dv = torch.zeros((B, Sk, H, D), dtype=torch.float32, device=dev)
+    for t, n, S_ in ((dq, "dq", Sq), (dk, "dk", Sk), (dv, "dv", Sk)):
+        _expect(_dev(t, n), n, (B, S_, H, D), torch.float32, dev)
     if workspace is None:
-        workspace = torch.empty((B * H * Sq,), dtype=torch.float32, device=q.device)
-    if workspace.dtype != torch.float32 or workspace.numel() < B * H * Sq:
-        raise ValueError("workspace must be float32 with at least B*H*Sq elements")
+        workspace = torch.empty((B * H * Sq,), dtype=torch.float32, device=dev)
     _dev(workspace, "workspace")
-    flags = THA_MASK_CAUSAL if causal else 0
-    kvp = None
-    if kv_len is not None:
-        kv_len = _dev(kv_len, "kv_len")
-        if kv_len.dtype != torch.int32:
-            raise ValueError("kv_len must be int32")
-        flags |= THA_MASK_KEY_PADDING
-        kvp = kv_len.data_ptr()
+    if workspace.dtype != torch.float32 or workspace.numel() < B * H * Sq or workspace.device != dev:
+        raise ValueError("workspace must be float32 on q's device with at least B*H*Sq elements")
+    kflag, kvp = _kv_len_arg(kv_len, B, dev)
+    flags = (THA_MASK_CAUSAL if causal else 0) | kflag
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     rc = _lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
@@ -237,16 +284,22 @@ def attn_merge_lse(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Te
     load_library()
     if len(o_parts) != len(lse_parts) or len(o_parts) == 0:
         raise ValueError("need matching, non-empty o_parts and lse_parts")
+    if len(o_parts) > THA_MAX_PARTS:
+        raise ValueError(f"at most {THA_MAX_PARTS} parts")
+    o0 = _dev(o_parts[0], "o_parts[0]")
+    B, S, H, D = _bshd(o0, "o_parts[0]")
+    dev = o0.device
     for i, (o, l) in enumerate(zip(o_parts, lse_parts)):
-        _dev(o, f"o_parts[{i}]"), _dev(l, f"lse_parts[{i}]")
-        if l.dtype != torch.float32:
-            raise ValueError("lse parts must be float32")
-    B, S, H, D = o_parts[0].shape
-    part_dt = _dt(o_parts[0].dtype)
+        _expect(_dev(o, f"o_parts[{i}]"), f"o_parts[{i}]", (B, S, H, D), o0.dtype, dev)
+        _expect(_dev(l, f"lse_parts[{i}]"), f"lse_parts[{i}]", (B, H, S), torch.float32, dev)
+    part_dt = _dt(o0.dtype)
     if out is None:
-        out = torch.empty((B, S, H, D), dtype=out_dtype or o_parts[0].dtype, device=o_parts[0].device)
+        out = torch.empty((B, S, H, D), dtype=out_dtype or o0.dtype, device=dev)
+    _expect(_dev(out, "out"), "out", (B, S, H, D), None, dev, (torch.bfloat16, torch.float32))
     if lse_out is None and return_lse:
-        lse_out = torch.empty((B, H, S), dtype=torch.float32, device=o_parts[0].device)
+        lse_out = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    if lse_out is not None:
+        _expect(_dev(lse_out, "lse_out"), "lse_out", (B, H, S), torch.float32, dev)
     rc = _lib.attn_merge_lse(len(o_parts), _ptrs(o_parts), _ptrs(lse_parts), part_dt, out.data_ptr(),
                              _dt(out.dtype), lse_out.data_ptr() if lse_out is not None else None, B, S, H, D,
                              _stream(out))
@@ -254,15 +307,27 @@ def attn_merge_lse(o_parts: Sequence[torch.Tensor], lse_parts: Sequence[torch.Te
     return (out, lse_out) if return_lse else out
 
 
+def _shard_list(shards: Sequence[torch.Tensor], name: str):
+    shards = [_dev(s, f"{name}[{i}]") for i, s in enumerate(shards)]
+    if not shards or len(shards) > THA_MAX_SHARDS:
+        raise ValueError(f"need 1 to {THA_MAX_SHARDS} {name}")
+    for i, s in enumerate(shards[1:], 1):
+        _expect(s, f"{name}[{i}]", shards[0].shape, shards[0].dtype, shards[0].device)
+    return shards
+
+
 def shard_permute(shards: Sequence[torch.Tensor], group: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """P sequence shards [B,S/P,H,D] -> head group `group` over the whole sequence [B,S,H/P,D]."""
     load_library()
-    shards = [_dev(s, f"shards[{i}]") for i, s in enumerate(shards)]
+    shards = _shard_list(shards, "shards")
     P = len(shards)
-    B, Sl, H, D = shards[0].shape
+    B, Sl, H, D = _bshd(shards[0], "shards[0]")
+    if H % P:
+        raise ValueError(f"heads ({H}) must be divisible by the shard count ({P})")
     if out is None:
-        out = torch.empty((B, Sl * P, H // P if P else H, D), dtype=shards[0].dtype, device=shards[0].device)
-    rc = _lib.shard_permute(_ptrs(shards), P, int(group), _dev(out, "out").data_ptr(), B, Sl * P, H, D,
+        out = torch.empty((B, Sl * P, H // P, D), dtype=shards[0].dtype, device=shards[0].device)
+    _expect(_dev(out, "out"), "out", (B, Sl * P, H // P, D), shards[0].dtype, shards[0].device)
+    rc = _lib.shard_permute(_ptrs(shards), P, int(group), out.data_ptr(), B, Sl * P, H, D,
                             shards[0].element_size(), _stream(out))
     _check(rc, "shard_permute")
     return out
@@ -272,9 +337,12 @@ def shard_unpermute(x: torch.Tensor, group: int, shards: Sequence[torch.Tensor])
     """Write head group `group` of x [B,S,H/P,D] back into the P sequence shards [B,S/P,H,D]."""
     load_library()
     x = _dev(x, "x")
-    shards = [_dev(s, f"shards[{i}]") for i, s in enumerate(shards)]
+    shards = _shard_list(shards, "shards")
     P = len(shards)
-    B, S, Hl, D = x.shape
+    B, S, Hl, D = _bshd(x, "x")
+    if S % P:
+        raise ValueError(f"sequence length ({S}) must be divisible by the shard count ({P})")
+    _expect(shards[0], "shards[0]", (B, S // P, Hl * P, D), x.dtype, x.device)
     rc = _lib.shard_unpermute(x.data_ptr(), P, int(group), _ptrs(shards), B, S, Hl * P, D, x.element_size(),
                               _stream(x))
     _check(rc, "shard_unpermute")
@@ -311,17 +379,18 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool
 
 def ulysses_share(q_shards: Sequence[torch.Tensor], k_shards: Sequence[torch.Tensor],
                   v_shards: Sequence[torch.Tensor], group: int, *, causal: bool = True,
-                  kv_len: Optional[torch.Tensor] = None, scale: Optional[float] = None):
+                  kv_len: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                  kernel: Optional[str] = None):
     """One GPU's Ulysses share: the P sequence shards [B,S/P,H,D] of Q, K and V are permuted to head
     group `group` over the whole sequence (shard_permute) and attended (attn_fwd).
     Returns (out [B,S,H/P,D], lse [B,H/P,S])."""
     q, k, v = (shard_permute(s, group) for s in (q_shards, k_shards, v_shards))
-    return attn_fwd(q, k, v, causal=causal, kv_len=kv_len, scale=scale)
+    return attn_fwd(q, k, v, causal=causal, kv_len=kv_len, scale=scale, kernel=kernel)
 
 
 def ring_share(q: torch.Tensor, k_chunks: Sequence[torch.Tensor], v_chunks: Sequence[torch.Tensor], *,
                q_pos0: int, k_pos0s: Sequence[int], causal: bool = True, scale: Optional[float] = None,
-               fused: bool = True, out_dtype: Optional[torch.dtype] = None):
+               fused: bool = True, out_dtype: Optional[torch.dtype] = None, kernel: Optional[str] = None):
     """One GPU's Ring share: the local Q chunk (first query at global position q_pos0) against K/V
     chunks that arrive in turn (first key of chunk t at k_pos0s[t]).  fused=True merges each chunk's
     result into a running fp32 (o, lse) in the attention epilogue (attn_fwd_ex with accumulate);
@@ -335,8 +404,8 @@ def ring_share(q: torch.Tensor, k_chunks: Sequence[torch.Tensor], v_chunks: Sequ
         lse = torch.full((B, H, Sq), float("-inf"), dtype=torch.float32, device=q.device)
         for kc, vc, kp in zip(k_chunks, v_chunks, k_pos0s):
             attn_fwd_ex(q, kc, vc, causal=causal, q_pos0=q_pos0, k_pos0=kp, scale=scale, out=o, lse=lse,
-                        accumulate=True)
+                        accumulate=True, kernel=kernel)
         return attn_merge_lse([o], [lse], out_dtype=out_dtype or q.dtype)
-    parts = [attn_fwd(q, kc, vc, causal=causal, q_pos0=q_pos0, k_pos0=kp, scale=scale, out_dtype=torch.float32)
-             for kc, vc, kp in zip(k_chunks, v_chunks, k_pos0s)]
+    parts = [attn_fwd(q, kc, vc, causal=causal, q_pos0=q_pos0, k_pos0=kp, scale=scale, out_dtype=torch.float32,
+                      kernel=kernel) for kc, vc, kp in zip(k_chunks, v_chunks, k_pos0s)]
     return attn_merge_lse([p[0] for p in parts], [p[1] for p in parts], out_dtype=out_dtype or q.dtype)

@@ -67,7 +67,10 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, int out_dt,
                float scale, const long long* st8, void* stream) {
   if (!q || !k || !v || !o) return THA_ERR_INVALID;
   if (B <= 0 || Sq <= 0 || Sk <= 0 || H <= 0 || D <= 0) return THA_ERR_INVALID;
-  if (flags & ~(unsigned)(THA_MASK_CAUSAL | THA_MASK_KEY_PADDING | THA_ACCUMULATE)) return THA_ERR_INVALID;
+  if (flags & ~(unsigned)(THA_MASK_CAUSAL | THA_MASK_KEY_PADDING | THA_ACCUMULATE | THA_KERNEL_MASK))
+    return THA_ERR_INVALID;
+  const unsigned kernel = flags & THA_KERNEL_MASK;
+  if (kernel > THA_KERNEL_SPLIT) return THA_ERR_INVALID;
   if ((flags & THA_MASK_KEY_PADDING) && !kv_len) return THA_ERR_INVALID;
   if (!isfinite(scale) || !(scale > 0.f)) return THA_ERR_INVALID;
   if (q_pos0 >= kMaxPos || q_pos0 <= -kMaxPos || k_pos0 >= kMaxPos || k_pos0 <= -kMaxPos) return THA_ERR_INVALID;
@@ -102,6 +105,10 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, int out_dt,
   a.q_bs = st8[0], a.q_rs = st8[1], a.k_bs = st8[2], a.k_rs = st8[3];
   a.v_bs = st8[4], a.v_rs = st8[5], a.o_bs = st8[6], a.o_rs = st8[7];
   a.accumulate = accumulate;
+  a.kernel = kernel == THA_KERNEL_NARROW ? tha::AttnArgs::kNarrow
+           : kernel == THA_KERNEL_WIDE   ? tha::AttnArgs::kWide
+           : kernel == THA_KERNEL_SPLIT  ? tha::AttnArgs::kSplit
+                                         : tha::AttnArgs::kAuto;
   hipStream_t s = (hipStream_t)stream;
   return hip_status(in_dt == THA_BF16 ? tha::launch_attn_bf16(a, s) : tha::launch_attn_f32(a, s));
 }
@@ -113,7 +120,7 @@ extern "C" {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, int out_dt, float* lse, int B, int Sq, int Sk,
              int H, int D, int in_dt, unsigned mask_flags, long long q_pos0, long long k_pos0, const int* kv_len,
              float scale, void* stream) {
-  if (mask_flags & THA_ACCUMULATE) return THA_ERR_INVALID;  // attn_fwd_ex only
+  if (mask_flags & (THA_ACCUMULATE | THA_KERNEL_MASK)) return THA_ERR_INVALID;  // attn_fwd_ex only
   const long long hd = (long long)H * D;
   const long long st8[8] = {Sq * hd, hd, Sk * hd, hd, Sk * hd, hd, Sq * hd, hd};
   return fwd_common(q, k, v, o, out_dt, lse, B, Sq, Sk, H, D, in_dt, mask_flags, q_pos0, k_pos0, kv_len, scale, st8,
@@ -142,6 +149,11 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   if ((int64_t)H * D > kMaxRowElems) return THA_ERR_UNSUPPORTED;
   if (in_dt == THA_BF16 && D != 128 && D != 64) return THA_ERR_UNSUPPORTED;
   if (in_dt == THA_F32 && D > 256) return THA_ERR_UNSUPPORTED;
+  if (in_dt == THA_BF16) {  // 16-byte loads of q, k, v, dout and 16-byte read-modify-writes of dq, dk, dv
+    const void* p16[7] = {q, k, v, dout, dq, dk, dv};
+    for (const void* p : p16)
+      if ((uintptr_t)p % 16) return THA_ERR_UNSUPPORTED;
+  }
   tha::AttnBwdArgs a;
   a.q = q, a.k = k, a.v = v, a.o = o, a.dout = dout, a.lse = lse;
   a.dq = dq, a.dk = dk, a.dv = dv, a.delta = workspace;

@@ -343,14 +343,13 @@ hipError_t launch_d(const AttnArgs& x, hipStream_t st) {
 // workgroup, one workgroup per CU) when its grid fills every CU at least twice; else the narrow
 // one (128 rows, two workgroups per CU) when its grid does; else the narrow kernel in split form
 // (two wavefront groups per workgroup share the key range), so small grids still put two
-// wavefronts on every SIMD.  THA_ATTN_D128_KERNEL=narrow|wide|split forces a choice.
+// wavefronts on every SIMD.  A caller's forced choice (AttnArgs::kernel) overrides this.
 enum class D128 { kNarrow, kWide, kSplit };
 
 D128 choose_d128(const AttnArgs& a) {
-  const char* force = getenv("THA_ATTN_D128_KERNEL");
-  if (force && strcmp(force, "wide") == 0) return D128::kWide;
-  if (force && strcmp(force, "narrow") == 0) return D128::kNarrow;
-  if (force && strcmp(force, "split") == 0) return D128::kSplit;
+  if (a.kernel == AttnArgs::kWide) return D128::kWide;
+  if (a.kernel == AttnArgs::kNarrow) return D128::kNarrow;
+  if (a.kernel == AttnArgs::kSplit) return D128::kSplit;
   static std::atomic<int> cu_count[64];  // per device, filled on first use (any thread may fill it)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return D128::kNarrow;

@@ -59,10 +59,12 @@ __device__ __forceinline__ void store1(void* p, int64_t i, float v) {
 // Vector path (D % 4 == 0, D <= 1024, 8/16-byte aligned rows): each thread owns one chunk of 4
 // consecutive elements of one row; a row is `lanes` consecutive threads of the block (lanes a power
 // of two, <= 256).  The data loads of the first 8 parts are issued before the lse reads, so a
-// workgroup waits for memory once rather than twice (lse, then data).  Every thread reads the row's
-// lse values before the block barrier and the row's single lse store comes after it, so lse_out may
-// be any lse_parts[k]; each output element is written by the thread that read it from every part, so
-// o_out may be any o_parts[k] of the same element type.
+// workgroup waits for memory once rather than twice (lse, then data).  In-place use: each output
+// element is written by the thread that read it from every part, so o_out may be any o_parts[k] of
+// the same element type; the row's single lse store comes after a block barrier that follows every
+// read of the row's lse values (the first 8 parts and the max before the first barrier; the later
+// parts, read while weighting, before a second barrier that only rows spanning several wavefronts
+// need), so lse_out may be any lse_parts[k].  No thread leaves before a barrier.
 template <typename PartT, typename OutT>
 __global__ void __launch_bounds__(kThreads) merge_vec_kernel(PartPtrs parts, int n, void* o_out, float* lse_out,
                                                             int64_t rows, int S, int H, int D, int lanes_log2) {
@@ -96,43 +98,44 @@ __global__ void __launch_bounds__(kThreads) merge_vec_kernel(PartPtrs parts, int
     }
     for (int k = kChunk; k < n; ++k) M = fmaxf(M, parts.lse[k][li]);
   }
-  __syncthreads();  // all lse reads of the block precede its lse writes (in-place safety)
-  if (!live) return;
-  if (M == -INFINITY) {
-    if (c < D) Vec4<OutT>::store(o_out, off, f32x4{0.f, 0.f, 0.f, 0.f});
-    if (lse_out && lane_in_row == 0) lse_out[li] = -INFINITY;
-    return;
-  }
+  __syncthreads();  // the lse reads above precede every lse write of the block
+  const bool work = live && M != -INFINITY;  // M = -inf: every part empty -> o = 0, lse = -inf
   float W = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int u = 0; u < kChunk; ++u)
-    if (u < n0) {
-      const float w = expf(l0[u] - M);
-      W += w;
-      if (c < D) acc += x[u] * w;
-    }
-  // further parts in chunks of 8: all loads of a chunk in flight before its weights are applied
-  for (int k0 = kChunk; k0 < n; k0 += kChunk) {
-    const int kn = min(kChunk, n - k0);
-    float w[kChunk];
-#pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
-      w[u] = 0.f;
-      if (u < kn) {
-        if (c < D) x[u] = Vec4<PartT>::load_nt(parts.o[k0 + u], off);
-        w[u] = expf(parts.lse[k0 + u][li] - M);
-      }
-    }
+  if (work) {
 #pragma unroll
     for (int u = 0; u < kChunk; ++u)
-      if (u < kn) {
-        W += w[u];
-        if (c < D) acc += x[u] * w[u];
+      if (u < n0) {
+        const float w = expf(l0[u] - M);
+        W += w;
+        if (c < D) acc += x[u] * w;
       }
+    // further parts in chunks of 8: all loads of a chunk in flight before its weights are applied
+    for (int k0 = kChunk; k0 < n; k0 += kChunk) {
+      const int kn = min(kChunk, n - k0);
+      float w[kChunk];
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u) {
+        w[u] = 0.f;
+        if (u < kn) {
+          if (c < D) x[u] = Vec4<PartT>::load_nt(parts.o[k0 + u], off);
+          w[u] = expf(parts.lse[k0 + u][li] - M);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kChunk; ++u)
+        if (u < kn) {
+          W += w[u];
+          if (c < D) acc += x[u] * w[u];
+        }
+    }
+    acc = acc * (1.0f / W);
   }
-  if (c < D) Vec4<OutT>::store(o_out, off, acc * (1.0f / W));
-  if (lse_out && lane_in_row == 0) lse_out[li] = M + logf(W);
+  if (act) Vec4<OutT>::store(o_out, off, acc);
+  // A row of more than 64 lanes spans several wavefronts: the reads of parts 8.. above, in every
+  // one of them, must precede the row's lse store (n and lanes are uniform over the grid).
+  if (n > kChunk && lanes_log2 > 6) __syncthreads();
+  if (live && lse_out && lane_in_row == 0) lse_out[li] = work ? M + logf(W) : -INFINITY;
 }
 
 // Scalar path (any D): a row is handled by `lanes` lanes of one wavefront (a power of two

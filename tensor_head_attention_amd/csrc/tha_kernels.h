@@ -33,6 +33,8 @@ struct AttnArgs {
   // k and v share one token stride (k_rs == v_rs).
   int64_t q_bs, q_rs, k_bs, k_rs, v_bs, v_rs, o_bs, o_rs;
   bool accumulate;  // o (fp32) and lse hold a running result: merge this call's result into them
+  // bf16, head size 128: which form of the kernel runs (kAuto = chosen by grid size)
+  enum Kernel { kAuto, kNarrow, kWide, kSplit } kernel = kAuto;
 };
 
 struct AttnBwdArgs {

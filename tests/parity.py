@@ -6,8 +6,6 @@ Tolerances (per the workload definitions):
                 over the whole output, on the same bf16-rounded inputs; lse <= 1e-4
 A row with no visible key must give o = 0 and lse = -inf on both sides.
 """
-import contextlib
-import os
 import sys
 
 import torch
@@ -54,21 +52,3 @@ def check_lse(dev_lse: torch.Tensor, ref: torch.Tensor, in_dtype: torch.dtype, w
         err = (l[fin] - ref[fin]).abs().max().item()
         say(f"  {what}: max-abs {err:.3e}")
         assert err <= TOL[in_dtype]["lse"], f"{what}: max-abs {err:.3e} > {TOL[in_dtype]['lse']}"
-
-
-@contextlib.contextmanager
-def d128_kernel(name):
-    """Force the bf16 head-size-128 attention kernel (narrow / wide / split; None = automatic choice)
-    for the calls inside, through the library's THA_ATTN_D128_KERNEL variable."""
-    old = os.environ.get("THA_ATTN_D128_KERNEL")
-    if name is None:
-        os.environ.pop("THA_ATTN_D128_KERNEL", None)
-    else:
-        os.environ["THA_ATTN_D128_KERNEL"] = name
-    try:
-        yield
-    finally:
-        if old is None:
-            os.environ.pop("THA_ATTN_D128_KERNEL", None)
-        else:
-            os.environ["THA_ATTN_D128_KERNEL"] = old

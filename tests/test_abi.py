@@ -30,8 +30,8 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = _declared_symbols()
-    assert {"attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_merge_lse", "shard_permute", "shard_unpermute", "tha_status_string",
-            "tha_version"} <= set(names)
+    assert {"attn_fwd", "attn_fwd_ex", "attn_bwd", "attn_merge_lse", "shard_permute", "shard_unpermute",
+            "tha_status_string", "tha_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     assert T.version() >= 100
@@ -98,7 +98,11 @@ def test_attn_fwd_ex_validation(lib):
     assert _fwdx(lib, q=None, strides=ok) == E
     assert _fwdx(lib, flags=T.THA_ACCUMULATE, out_dt=1, strides=ok) == E   # accumulate needs an fp32 o
     assert _fwdx(lib, flags=T.THA_ACCUMULATE, out_dt=0, lse=None, strides=ok) == E  # ... and an lse
-    assert _fwdx(lib, flags=8, strides=ok) == E                             # unknown flag bit
+    assert _fwdx(lib, flags=64, strides=ok) == E                            # unknown flag bit
+    assert _fwdx(lib, flags=4 << 3, strides=ok) == E                        # unknown kernel form
+    assert _attn(lib, flags=T.THA_KERNEL_NARROW) == E                      # attn_fwd takes no kernel form
+    for kf in (T.THA_KERNEL_NARROW, T.THA_KERNEL_WIDE, T.THA_KERNEL_SPLIT):  # valid forms pass to the next check
+        assert _fwdx(lib, flags=kf, q=None, strides=ok) == E
     bad = list(ok); bad[1] = hd - 8                                         # token stride < H*D
     assert _fwdx(lib, strides=bad) == E
     bad = list(ok); bad[0] = 3 * hd                                         # batches overlap
@@ -134,6 +138,8 @@ def test_attn_bwd_validation(lib):
     assert _bwd(lib, D=96) == U
     assert _bwd(lib, in_dt=0, D=300) == U
     assert _bwd(lib, H=1 << 20, D=128) == U
+    for name in ("q", "k", "v", "do", "dq", "dk", "dv"):                  # bf16 path: 16-byte aligned vectors
+        assert _bwd(lib, **{name: ctypes.c_void_p(0x1008)}) == U, name
 
 
 def _ptr_arr(n, val=0x1000):

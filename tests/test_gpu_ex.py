@@ -12,7 +12,7 @@ import torch
 import oracle
 import tensor_head_attention_amd as T
 import tha_workloads as W
-from parity import DEV, check_lse, check_out, d128_kernel, say, to_dev
+from parity import DEV, check_lse, check_out, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -33,10 +33,9 @@ def test_packed_qkv_views(B, S, H, D, dt, causal, kernel):
     ref, ref_lse = oracle.attention(q, k, v, causal=causal)
     dev = qkv.to(DEV)
     qv, kv_, vv = dev[:, :, 0], dev[:, :, 1], dev[:, :, 2]   # views, token stride 3*H*D
-    with d128_kernel(kernel):
-        out, lse = T.attn_fwd_ex(qv, kv_, vv, causal=causal)
-        base, base_lse = T.attn_fwd(*to_dev(q, k, v), causal=causal)
-        torch.cuda.synchronize()
+    out, lse = T.attn_fwd_ex(qv, kv_, vv, causal=causal, kernel=kernel)
+    base, base_lse = T.attn_fwd(*to_dev(q, k, v), causal=causal, kernel=kernel)
+    torch.cuda.synchronize()
     assert torch.equal(out, base) and torch.equal(lse, base_lse)
     check_out(out, ref, dt)
     check_lse(lse, ref_lse, dt)
@@ -52,11 +51,10 @@ def test_head_subset_views_and_strided_output(kernel):
     qv, kv_, vv = (t[:, :, 2:5] for t in big)
     o_big = torch.full((B, S, 6, D), 7.0, dtype=torch.float32, device=DEV)
     lse = torch.empty((B, 3, S), dtype=torch.float32, device=DEV)
-    with d128_kernel(kernel):
-        T.attn_fwd_ex(qv, kv_, vv, causal=True, out=o_big[:, :, 1:4], lse=lse)
-        base, base_lse = T.attn_fwd(qv.contiguous(), kv_.contiguous(), vv.contiguous(), causal=True,
-                                    out_dtype=torch.float32)
-        torch.cuda.synchronize()
+    T.attn_fwd_ex(qv, kv_, vv, causal=True, out=o_big[:, :, 1:4], lse=lse, kernel=kernel)
+    base, base_lse = T.attn_fwd(qv.contiguous(), kv_.contiguous(), vv.contiguous(), causal=True,
+                                out_dtype=torch.float32, kernel=kernel)
+    torch.cuda.synchronize()
     assert torch.equal(o_big[:, :, 1:4], base) and torch.equal(lse, base_lse)
     assert torch.all(o_big[:, :, 0] == 7.0) and torch.all(o_big[:, :, 4:] == 7.0)
     ref, ref_lse = oracle.attention(*(t.cpu() for t in (qv.contiguous(), kv_.contiguous(), vv.contiguous())),
@@ -83,20 +81,19 @@ def test_fused_ring_step(D, dt, kernel):
     o = torch.full((1, Sc, H, D), float("nan"), dtype=torch.float32, device=DEV)  # never read while lse = -inf
     lse = torch.full((1, H, Sc), float("-inf"), dtype=torch.float32, device=DEV)
     parts = []
-    with d128_kernel(kernel):
-        for t in range(P):
-            kc, vc = kd[:, t * Sc:(t + 1) * Sc], vd[:, t * Sc:(t + 1) * Sc]   # views into the full K/V
-            if t == 4:
-                before = (o.clone(), lse.clone())
-            T.attn_fwd_ex(qd, kc, vc, causal=True, q_pos0=qp, k_pos0=t * Sc, out=o, lse=lse, accumulate=True)
-            if t == 4:  # the chunk lies wholly in the queries' future: the running result is unchanged
-                torch.cuda.synchronize()
-                assert torch.equal(o, before[0]) and torch.equal(lse, before[1])
-            parts.append(T.attn_fwd(qd, kc.contiguous(), vc.contiguous(), causal=True, q_pos0=qp, k_pos0=t * Sc,
-                                    out_dtype=torch.float32))
-        merged, merged_lse = T.attn_merge_lse([p[0] for p in parts], [p[1] for p in parts],
-                                              out_dtype=torch.float32)
-        torch.cuda.synchronize()
+    for t in range(P):
+        kc, vc = kd[:, t * Sc:(t + 1) * Sc], vd[:, t * Sc:(t + 1) * Sc]   # views into the full K/V
+        if t == 4:
+            before = (o.clone(), lse.clone())
+        T.attn_fwd_ex(qd, kc, vc, causal=True, q_pos0=qp, k_pos0=t * Sc, out=o, lse=lse, accumulate=True, kernel=kernel)
+        if t == 4:  # the chunk lies wholly in the queries' future: the running result is unchanged
+            torch.cuda.synchronize()
+            assert torch.equal(o, before[0]) and torch.equal(lse, before[1])
+        parts.append(T.attn_fwd(qd, kc.contiguous(), vc.contiguous(), causal=True, q_pos0=qp, k_pos0=t * Sc,
+                                out_dtype=torch.float32, kernel=kernel))
+    merged, merged_lse = T.attn_merge_lse([p[0] for p in parts], [p[1] for p in parts],
+                                          out_dtype=torch.float32)
+    torch.cuda.synchronize()
     assert torch.isfinite(o).all()
     check_out(o, ref, dt)
     check_lse(lse, ref_lse, dt)

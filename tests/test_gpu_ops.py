@@ -126,3 +126,25 @@ def test_merge_in_place_any_part(dt, D):
     assert torch.equal(od[-1], expect) and torch.equal(ld[-1], expect_lse)
     check_out(od[-1], ref, dt)
     check_lse(ld[-1], ref_lse, torch.float32)
+
+
+@pytest.mark.parametrize("n", [9, 17, 64])
+@pytest.mark.parametrize("D", [512, 1024])
+def test_merge_in_place_rows_across_wavefronts(n, D):
+    """Rows of 512 or 1024 elements span two or four wavefronts of the vector kernel, and parts
+    beyond the eighth are weighted after the first barrier: with lse_out (and o_out) equal to the
+    last part, every wavefront of a row must read that part's lse before the row's lse store."""
+    B, S, H = 1, 40, 2
+    say(f"merge in place n{n} D{D} (rows across wavefronts)")
+    # lse values within a few units of each other: the merged lse exceeds every part's by about
+    # log(n), so a weight read after the store (exp(lse_out - M) for the last part) would be off
+    # by a factor of about n
+    os_, ls_ = _parts(n, B, S, H, D, seed=n * 7 + D, spread=1.0)
+    ref, ref_lse = oracle.merge_lse([o.double() for o in os_], [l.double() for l in ls_])
+    od, ld = to_dev(*os_), to_dev(*ls_)
+    expect, expect_lse = T.attn_merge_lse(od, ld, out_dtype=torch.float32)
+    T.attn_merge_lse(od, ld, out=od[-1], lse_out=ld[-1])
+    torch.cuda.synchronize()
+    assert torch.equal(od[-1], expect) and torch.equal(ld[-1], expect_lse)
+    check_out(od[-1], ref, torch.float32)
+    check_lse(ld[-1], ref_lse, torch.float32)

@@ -9,7 +9,7 @@ import torch
 import oracle
 import tensor_head_attention_amd as T
 import tha_workloads as W
-from parity import DEV, check_lse, check_out, d128_kernel, say, to_dev
+from parity import DEV, check_lse, check_out, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -37,18 +37,17 @@ def test_fwd_position_shift(kern):
     say(f"positions fwd {_kid(kern)}")
     q, k, v = _inputs(D, dt, seed=901 + D)
     qd, kd, vd = to_dev(q, k, v)
-    with d128_kernel(kn):
-        o0, l0 = T.attn_fwd(qd, kd, vd, causal=True, q_pos0=37, k_pos0=5, out_dtype=torch.float32)
-        for s in SHIFTS:
-            o1, l1 = T.attn_fwd(qd, kd, vd, causal=True, q_pos0=37 + s, k_pos0=5 + s, out_dtype=torch.float32)
-            torch.cuda.synchronize()
-            assert torch.equal(o0, o1) and torch.equal(l0, l1), f"shift {s}"
-        # a query chunk far after every key sees them all: the non-causal result
-        on, ln = T.attn_fwd(qd, kd, vd, out_dtype=torch.float32)
-        oa, la = T.attn_fwd(qd, kd, vd, causal=True, q_pos0=BIG, k_pos0=-BIG, out_dtype=torch.float32)
-        # and one far before every key sees none
-        oz, lz = T.attn_fwd(qd, kd, vd, causal=True, q_pos0=-BIG, k_pos0=BIG, out_dtype=torch.float32)
+    o0, l0 = T.attn_fwd(qd, kd, vd, causal=True, q_pos0=37, k_pos0=5, out_dtype=torch.float32, kernel=kn)
+    for s in SHIFTS:
+        o1, l1 = T.attn_fwd(qd, kd, vd, causal=True, q_pos0=37 + s, k_pos0=5 + s, out_dtype=torch.float32, kernel=kn)
         torch.cuda.synchronize()
+        assert torch.equal(o0, o1) and torch.equal(l0, l1), f"shift {s}"
+    # a query chunk far after every key sees them all: the non-causal result
+    on, ln = T.attn_fwd(qd, kd, vd, out_dtype=torch.float32, kernel=kn)
+    oa, la = T.attn_fwd(qd, kd, vd, causal=True, q_pos0=BIG, k_pos0=-BIG, out_dtype=torch.float32, kernel=kn)
+    # and one far before every key sees none
+    oz, lz = T.attn_fwd(qd, kd, vd, causal=True, q_pos0=-BIG, k_pos0=BIG, out_dtype=torch.float32, kernel=kn)
+    torch.cuda.synchronize()
     assert torch.equal(oa, on) and torch.equal(la, ln)
     assert torch.count_nonzero(oz).item() == 0 and bool(torch.all(lz == float("-inf")))
     ref, ref_lse = oracle.attention(q, k, v, causal=True, q_pos0=37, k_pos0=5)

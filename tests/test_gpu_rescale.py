@@ -14,7 +14,7 @@ import torch
 import oracle
 import tensor_head_attention_amd as T
 import tha_workloads as W
-from parity import check_lse, check_out, d128_kernel, say, to_dev
+from parity import check_lse, check_out, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -61,9 +61,8 @@ def test_rescale_matches_oracle(kern, recipe, causal):
     q, k, v = inputs(recipe, 2, 300, 1100, 2, D, dt, seed=501 + D)
     ref, ref_lse = oracle.attention(q, k, v, causal=causal, q_pos0=800)
     qd, kd, vd = to_dev(q, k, v)
-    with d128_kernel(kn):
-        out, lse = T.attn_fwd(qd, kd, vd, causal=causal, q_pos0=800, out_dtype=torch.float32)
-        torch.cuda.synchronize()
+    out, lse = T.attn_fwd(qd, kd, vd, causal=causal, q_pos0=800, out_dtype=torch.float32, kernel=kn)
+    torch.cuda.synchronize()
     check_out(out, ref, dt)
     if dt == torch.float32:
         # the spikes put lse near 50 for some rows, where one fp32 ulp is ~4e-6: the fp32 bound of
@@ -87,9 +86,8 @@ def test_rescale_narrow_wide_bitwise(recipe):
     qd, kd, vd = to_dev(q, k, v)
     res = {}
     for kn in ("narrow", "wide"):
-        with d128_kernel(kn):
-            res[kn] = T.attn_fwd(qd, kd, vd, causal=True, q_pos0=1000, out_dtype=torch.float32)
-            torch.cuda.synchronize()
+        res[kn] = T.attn_fwd(qd, kd, vd, causal=True, q_pos0=1000, out_dtype=torch.float32, kernel=kn)
+        torch.cuda.synchronize()
     assert torch.equal(res["narrow"][0], res["wide"][0]) and torch.equal(res["narrow"][1], res["wide"][1])
     ref, ref_lse = oracle.attention(q, k, v, causal=True, q_pos0=1000)
     check_out(res["wide"][0], ref, torch.bfloat16)

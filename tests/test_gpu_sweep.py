@@ -10,7 +10,7 @@ import torch
 import oracle
 import tensor_head_attention_amd as T
 import tha_workloads as W
-from parity import DEV, check_lse, check_out, d128_kernel, say, to_dev
+from parity import DEV, check_lse, check_out, say, to_dev
 from test_gpu_bwd import check_grad
 
 pytestmark = pytest.mark.gpu
@@ -55,9 +55,9 @@ def test_fwd_sweep(case, D, kernel):
     ref, ref_lse = oracle.attention(q, k, v, causal=causal, q_pos0=qp, k_pos0=kp, kv_len=kv)
     qd, kd, vd = to_dev(q, k, v)
     kvd = kv.to(DEV) if kv is not None else None
-    with d128_kernel(kernel):
-        out, lse = T.attn_fwd(qd, kd, vd, causal=causal, q_pos0=qp, k_pos0=kp, kv_len=kvd, out_dtype=torch.float32)
-        torch.cuda.synchronize()
+    out, lse = T.attn_fwd(qd, kd, vd, causal=causal, q_pos0=qp, k_pos0=kp, kv_len=kvd, out_dtype=torch.float32,
+                          kernel=kernel)
+    torch.cuda.synchronize()
     check_out(out, ref, torch.bfloat16)
     check_lse(lse, ref_lse, torch.bfloat16)
 
@@ -102,11 +102,10 @@ def test_fused_ring_sweep(kernel, seed):
     qd, kd, vd = to_dev(q, k, v)
     o = torch.zeros((B, Sq, H, D), dtype=torch.float32, device=DEV)
     lse = torch.full((B, H, Sq), float("-inf"), dtype=torch.float32, device=DEV)
-    with d128_kernel(kernel):
-        for t in range(P):
-            kvc = (kv - t * Sc).clamp(0, Sc).to(torch.int32).to(DEV)
-            T.attn_fwd_ex(qd, kd[:, t * Sc:(t + 1) * Sc], vd[:, t * Sc:(t + 1) * Sc], causal=True, q_pos0=qp,
-                          k_pos0=t * Sc, kv_len=kvc, out=o, lse=lse, accumulate=True)
-        torch.cuda.synchronize()
+    for t in range(P):
+        kvc = (kv - t * Sc).clamp(0, Sc).to(torch.int32).to(DEV)
+        T.attn_fwd_ex(qd, kd[:, t * Sc:(t + 1) * Sc], vd[:, t * Sc:(t + 1) * Sc], causal=True, q_pos0=qp,
+                      k_pos0=t * Sc, kv_len=kvc, out=o, lse=lse, accumulate=True, kernel=kernel)
+    torch.cuda.synchronize()
     check_out(o, ref, torch.bfloat16)
     check_lse(lse, ref_lse, torch.bfloat16)

@@ -10,7 +10,7 @@ import torch
 import oracle
 import tensor_head_attention_amd as T
 import tha_workloads as W
-from parity import DEV, check_lse, check_out, d128_kernel, say, to_dev
+from parity import DEV, check_lse, check_out, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -83,9 +83,9 @@ def test_workload3_ulysses_share():
     q, k, v = (grouped[n][1] for n in ("q", "k", "v"))
     out, lse = T.attn_fwd(qd, kd, vd, causal=True)  # the wide kernel, as timed
     torch.cuda.synchronize()
-    with d128_kernel("narrow"):  # the other head-size-128 kernel gives the same bits
-        out_n, lse_n = T.attn_fwd(qd, kd, vd, causal=True)
-        torch.cuda.synchronize()
+    # the other head-size-128 kernel gives the same bits
+    out_n, lse_n = T.attn_fwd(qd, kd, vd, causal=True, kernel="narrow")
+    torch.cuda.synchronize()
     assert torch.equal(out_n, out) and torch.equal(lse_n, lse)
     del out_n, lse_n
     Hl = H // P
@@ -132,9 +132,8 @@ def test_workload5_padded_batch():
     qd, kd, vd, kvd = to_dev(q, k, v, kv)
     out, lse = T.attn_fwd(qd, kd, vd, kv_len=kvd)
     torch.cuda.synchronize()
-    with d128_kernel("narrow"):
-        out_n, lse_n = T.attn_fwd(qd, kd, vd, kv_len=kvd)
-        torch.cuda.synchronize()
+    out_n, lse_n = T.attn_fwd(qd, kd, vd, kv_len=kvd, kernel="narrow")
+    torch.cuda.synchronize()
     assert torch.equal(out_n, out) and torch.equal(lse_n, lse)
     del out_n, lse_n
     lens = kv.tolist()
