@@ -55,8 +55,11 @@ def _load():
         lib.oracle_attention_backward.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64,
                                                   ctypes.c_int, i64, i64, vp, ctypes.c_double, dp, dp, dp,
                                                   ctypes.c_int]
+        lib.oracle_all_to_all.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, vp]
         for f in (lib.oracle_attention, lib.oracle_attention_bruteforce, lib.oracle_merge_lse,
-                  lib.oracle_shard_permute, lib.oracle_shard_unpermute, lib.oracle_attention_backward):
+                  lib.oracle_shard_permute, lib.oracle_shard_unpermute, lib.oracle_attention_backward,
+                  lib.oracle_all_to_all):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -222,3 +225,28 @@ def shard_unpermute(groups: Sequence[torch.Tensor]):
     if rc != 0:
         raise ValueError("oracle_shard_unpermute rejected its arguments")
     return shards
+
+
+def all_to_all(inputs: Sequence[torch.Tensor], rank: int, scatter_dim: int, gather_dim: int) -> torch.Tensor:
+    """What rank `rank` holds after the all-to-all of the P ranks' tensors `inputs` (one shape, one
+    dtype): each input split into P chunks along scatter_dim, chunk r sent to rank r, the received
+    chunks concatenated in rank order along gather_dim."""
+    ins = [_host(t) for t in inputs]
+    P = len(ins)
+    shape = list(ins[0].shape)
+    if any(list(t.shape) != shape or t.dtype != ins[0].dtype for t in ins):
+        raise ValueError("inputs must share one shape and dtype")
+    nd = len(shape)
+    sd, gd = scatter_dim % nd, gather_dim % nd
+    if shape[sd] % P:
+        raise ValueError("the scatter dim must be divisible by the rank count")
+    out_shape = list(shape)
+    out_shape[sd] //= P
+    out_shape[gd] *= P
+    out = torch.empty(out_shape, dtype=ins[0].dtype)
+    sh = (ctypes.c_int64 * nd)(*shape)
+    rc = _load().oracle_all_to_all(_ptr_array([t.data_ptr() for t in ins]), P, int(rank), nd, sh, sd, gd,
+                                   ins[0].element_size(), out.data_ptr())
+    if rc != 0:
+        raise ValueError("oracle_all_to_all rejected its arguments")
+    return out

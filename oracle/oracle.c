@@ -339,6 +339,55 @@ int oracle_shard_unpermute(const void* const* groups, int P, int64_t B, int64_t 
   return 0;
 }
 
+/*
+ * oracle_all_to_all: the local effect of an all-to-all with a scatter dim and a
+ * gather dim ("Support deepspeed sequence parallel", PR body: the sequence
+ * all-to-all is parameterised by a scatter index and a gather index, and
+ * all_to_all_single replaces all_to_all).  Each of the P ranks holds a tensor of
+ * shape `shape` (ndim dims, row-major); rank i splits its tensor into P equal
+ * chunks along scatter_dim and sends chunk r to rank r; rank r concatenates what
+ * it receives, in rank order, along gather_dim.  So rank r's result has
+ * shape[scatter_dim] / P at scatter_dim and shape[gather_dim] * P at gather_dim,
+ * and its element at index o (a multi-index) is input i's element at index o
+ * with  o[gather_dim] replaced by o[gather_dim] - i * shape[gather_dim]  (i =
+ * o[gather_dim] / shape[gather_dim])  and  o[scatter_dim] replaced by
+ * r * shape[scatter_dim] / P + o[scatter_dim].  Written out per element with
+ * multi-indices.  Returns 0, or -1 on a bad argument.
+ */
+int oracle_all_to_all(const void* const* inputs, int P, int rank, int ndim, const int64_t* shape, int scatter_dim,
+                      int gather_dim, int elem_bytes, void* out) {
+  if (!inputs || !out || !shape || P < 1 || rank < 0 || rank >= P || ndim < 1 || ndim > 8 || elem_bytes <= 0)
+    return -1;
+  if (scatter_dim < 0 || scatter_dim >= ndim || gather_dim < 0 || gather_dim >= ndim || scatter_dim == gather_dim)
+    return -1;
+  int64_t in_shape[8], out_shape[8], total = 1;
+  for (int d = 0; d < ndim; ++d) {
+    if (shape[d] <= 0) return -1;
+    in_shape[d] = out_shape[d] = shape[d];
+    total *= shape[d];
+  }
+  if (in_shape[scatter_dim] % P != 0) return -1;
+  out_shape[scatter_dim] = in_shape[scatter_dim] / P;
+  out_shape[gather_dim] = in_shape[gather_dim] * P;
+  int64_t o[8], src[8];
+  for (int64_t e = 0; e < total; ++e) { /* output elements in row-major order (P * total/P of them) */
+    int64_t rem = e;
+    for (int d = ndim - 1; d >= 0; --d) {
+      o[d] = rem % out_shape[d];
+      rem /= out_shape[d];
+    }
+    const int64_t i = o[gather_dim] / in_shape[gather_dim];
+    for (int d = 0; d < ndim; ++d) src[d] = o[d];
+    src[gather_dim] = o[gather_dim] - i * in_shape[gather_dim];
+    src[scatter_dim] = (int64_t)rank * out_shape[scatter_dim] + o[scatter_dim];
+    int64_t flat = 0;
+    for (int d = 0; d < ndim; ++d) flat = flat * in_shape[d] + src[d];
+    memcpy((char*)out + (size_t)e * (size_t)elem_bytes, (const char*)inputs[i] + (size_t)flat * (size_t)elem_bytes,
+           (size_t)elem_bytes);
+  }
+  return 0;
+}
+
 /* ---- attention backward (the vector-Jacobian product of attention) ------ */
 
 /*

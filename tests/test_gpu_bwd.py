@@ -163,17 +163,27 @@ def test_bwd_workload2_causal_4k_full():
     check_grad(dv, rv, torch.bfloat16, "dv")
 
 
-def test_bwd_ulysses_share_32k_sampled():
-    """The Ulysses share's attention (causal S32768, 8 heads x 128) at full size: sampled dq rows
-    against the oracle (row i of dq depends on query row i only, so the oracle runs each sampled
-    row as a one-row call at its position), and for dk / dv the closed forms that hold at any
-    size: per (b, h) the keys' dk sum to 0, and the keys' dv sum to the sum of dout over rows."""
-    say("bwd Ulysses share 32k")
+@pytest.fixture(scope="module")
+def bwd32k():
+    """The Ulysses share's attention (causal S32768, 8 heads x 128, bf16) and its full-size backward
+    on the device, as a user runs it (attn_fwd, then attn_bwd)."""
+    say("bwd Ulysses share 32k: device forward and backward")
     g = W.generator(93)
     S, H, D = 32768, 8, 128
     q, k, v, dout = (W.randn((1, S, H, D), g, torch.bfloat16) for _ in range(4))
     dq, dk, dv = _device_bwd(q, k, v, dout, True, 0, 0, None)
     torch.cuda.synchronize()
+    yield dict(S=S, H=H, D=D, g=g, host=(q, k, v, dout), dev=(dq, dk, dv))
+
+
+def test_bwd_ulysses_share_32k_sampled(bwd32k):
+    """Sampled dq rows against the oracle (row i of dq depends on query row i only, so the oracle
+    runs each sampled row as a one-row call at its position), and for dk / dv the closed forms that
+    hold at any size: per (b, h) the keys' dk sum to 0, and the keys' dv sum to the sum of dout over
+    rows."""
+    S, g = bwd32k["S"], bwd32k["g"]
+    q, k, v, dout = bwd32k["host"]
+    dq, dk, dv = bwd32k["dev"]
     rows = [0, 1, 63, 64, 127, 128, 4095, 4096, 16383, 16384, 32766, 32767] + \
         torch.randint(0, S, (6,), generator=g).tolist()
     dq_c = dq.cpu().double()
@@ -188,3 +198,37 @@ def test_bwd_ulysses_share_32k_sampled():
     assert dk_sum.abs().max().item() <= 1e-2 * dk.abs().max().item() * math.sqrt(S)
     assert (dv_sum - dout_sum).abs().max().item() <= 2e-2 * dout_sum.abs().max().item()
     assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
+
+
+LAST = 4096  # the last query rows: keys at or after their first position see no other query row
+
+
+@pytest.mark.parametrize("h", list(range(8)))
+def test_bwd_ulysses_share_32k_last_chunk(bwd32k, h):
+    """Every element of dq for the last 4096 query rows, and of dk and dv for the last 4096 keys, of
+    head h at full size.  Under the causal mask key j receives gradient only from query rows i >= j,
+    so the oracle's backward of query rows S-4096.. against ALL keys gives those keys' dk and dv in
+    full (and those rows' dq).  The oracle runs on blocks of 256 query rows in parallel host threads
+    (one single-threaded call each; the test adds the blocks' dk / dv in fp64)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from parity import host_threads
+    S = bwd32k["S"]
+    q, k, v, dout = bwd32k["host"]
+    dq, dk, dv = bwd32k["dev"]
+    say(f"bwd Ulysses share 32k: head {h}, rows and keys {S - LAST}..{S - 1} against the oracle")
+    kh, vh = (t[:, :, h:h + 1].contiguous() for t in (k, v))
+    blk = 256
+
+    def block(r0):
+        qb, db = (t[:, r0:r0 + blk, h:h + 1].contiguous() for t in (q, dout))
+        return oracle.attention_backward(qb, kh, vh, db, causal=True, q_pos0=r0, k_pos0=0, nthreads=1)
+
+    with ThreadPoolExecutor(max_workers=host_threads()) as ex:
+        res = list(ex.map(block, range(S - LAST, S, blk)))
+    rq = torch.cat([r[0] for r in res], dim=1)
+    rk = sum(r[1][:, S - LAST:] for r in res)
+    rv = sum(r[2][:, S - LAST:] for r in res)
+    check_grad(dq[:, S - LAST:, h:h + 1], rq, torch.bfloat16, f"dq rows {S - LAST}.. head {h}")
+    check_grad(dk[:, S - LAST:, h:h + 1], rk, torch.bfloat16, f"dk keys {S - LAST}.. head {h}")
+    check_grad(dv[:, S - LAST:, h:h + 1], rv, torch.bfloat16, f"dv keys {S - LAST}.. head {h}")

@@ -322,6 +322,73 @@ def test_permute_matches_concat_then_slice():
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("case", json.load(open(os.path.join(GOLDEN, "hand_examples.json")))["all_to_all"],
+                         ids=["ulysses_forward", "ulysses_return", "seq_first_with_middle_dim"])
+def test_hand_example_all_to_all(case):
+    """Hand-derived all-to-all layouts (values worked out by hand in the derivation strings)."""
+    ins = [torch.tensor(x, dtype=torch.int32) for x in case["inputs"]]
+    for r in range(case["P"]):
+        out = oracle.all_to_all(ins, r, case["scatter_dim"], case["gather_dim"])
+        assert out.tolist() == case["outputs"][r]
+
+
+# (shape per rank, P, scatter dim, gather dim): Ulysses forward/return on [B,S,H,D], the
+# sequence-first [S,B,H,D] layout, packed QKV [B,S,3,H,D], 1-byte and 8-byte elements, and dims at
+# both ends of the shape
+A2A_CASES = [((2, 3, 8, 4), 4, 2, 1, torch.bfloat16), ((2, 12, 2, 4), 4, 1, 2, torch.bfloat16),
+             ((3, 2, 6, 5), 3, 2, 0, torch.float32), ((2, 3, 3, 4, 2), 2, 3, 1, torch.bfloat16),
+             ((4, 6), 2, 0, 1, torch.int8), ((5, 2, 4), 4, 2, 0, torch.float64),
+             ((2, 2, 2, 2, 2, 2, 2, 4), 2, 7, 0, torch.int16)]
+
+
+def _a2a_inputs(shape, P, dtype, seed):
+    g = W.generator(seed)
+    if dtype in (torch.int8, torch.int16):
+        return [torch.randint(-100, 100, shape, generator=g, dtype=dtype) for _ in range(P)]
+    return [W.randn(shape, g, torch.float32).to(dtype) for _ in range(P)]
+
+
+@pytest.mark.parametrize("shape,P,sd,gd,dtype", A2A_CASES)
+def test_all_to_all_matches_split_and_cat(shape, P, sd, gd, dtype):
+    """The definition with library routines: rank r's result = concatenation along the gather dim,
+    in rank order, of chunk r of every rank's tensor split into P parts along the scatter dim
+    (torch.tensor_split / torch.cat, the all_to_all of "Support deepspeed sequence parallel")."""
+    ins = _a2a_inputs(shape, P, dtype, seed=len(shape) * 10 + sd)
+    for r in range(P):
+        ref = torch.cat([torch.tensor_split(x, P, dim=sd)[r] for x in ins], dim=gd)
+        got = oracle.all_to_all(ins, r, sd, gd)
+        assert got.shape == ref.shape and torch.equal(got.view(torch.uint8), ref.contiguous().view(torch.uint8))
+
+
+@pytest.mark.parametrize("shape,P,sd,gd,dtype", A2A_CASES)
+def test_all_to_all_round_trip(shape, P, sd, gd, dtype):
+    """The all-to-all with the dims swapped undoes it: every rank gets its own tensor back."""
+    ins = _a2a_inputs(shape, P, dtype, seed=len(shape) * 10 + gd + 1)
+    mid = [oracle.all_to_all(ins, r, sd, gd) for r in range(P)]
+    for r in range(P):
+        back = oracle.all_to_all(mid, r, gd, sd)
+        assert torch.equal(back.view(torch.uint8), ins[r].view(torch.uint8))
+
+
+def test_all_to_all_ulysses_case_is_shard_permute():
+    """Scatter heads (dim 2), gather seq (dim 1) on [B, S/P, H, D] shards is shard_permute."""
+    P, B, S, H, D = 4, 2, 12, 8, 3
+    ins = _a2a_inputs((B, S // P, H, D), P, torch.bfloat16, seed=21)
+    for r in range(P):
+        assert torch.equal(oracle.all_to_all(ins, r, 2, 1).view(torch.int16),
+                           oracle.shard_permute(ins, r).view(torch.int16))
+
+
+def test_all_to_all_rejects_bad_dims():
+    ins = _a2a_inputs((4, 6), 2, torch.float32, seed=1)
+    with pytest.raises(ValueError):
+        oracle.all_to_all(ins, 0, 1, 1)       # scatter dim == gather dim
+    with pytest.raises(ValueError):
+        oracle.all_to_all(_a2a_inputs((3, 6), 2, torch.float32, 1), 0, 0, 1)  # 3 rows over 2 ranks
+    with pytest.raises(ValueError):
+        oracle.all_to_all(ins, 2, 0, 1)       # rank out of range
+
+
 def test_workload_one_full_check():
     """Workload 1 end to end on the oracle: two-pass == brute force == torch fp64 MHA."""
     inp, p = W.workload_inputs(1)
