@@ -244,6 +244,35 @@ THA_API int shard_permute(const void* const* shards, int P, int group, void* out
 THA_API int shard_unpermute(const void* in, int P, int group, void* const* shards, int B, int S, int H, int D,
                     int elem_bytes, void* stream);
 
+/*
+ * shard_all_to_all -- the local layout of an all-to-all with a general scatter dim and gather
+ * dim ("Support deepspeed sequence parallel", PR body: the sequence all-to-all takes a scatter
+ * index and a gather index, and uses all_to_all_single into one contiguous output).  Each of P
+ * ranks holds a tensor of shape `shape`; rank i splits it into P equal chunks along scatter_dim
+ * and sends chunk r to rank r; rank r concatenates the chunks it receives, in rank order, along
+ * gather_dim.  This call computes what rank `rank` holds afterwards, from all P tensors:
+ *
+ *   inputs  host array of P device pointers, each a contiguous row-major tensor of `shape`
+ *   shape   host array of ndim sizes (1 <= ndim <= 8), every size >= 1
+ *   out     contiguous, of `shape` with shape[scatter_dim] / P at scatter_dim and
+ *           shape[gather_dim] * P at gather_dim:
+ *           out[.., i*shape[gather_dim] + t (gather_dim), .., hh (scatter_dim), ..]
+ *             = inputs[i][.., t, .., rank*shape[scatter_dim]/P + hh, ..]
+ *
+ * The Ulysses cases on [B, S, H, D]: scatter_dim 2, gather_dim 1 is shard_permute (the inputs
+ * are the sequence shards); scatter_dim 1, gather_dim 2 is the return all-to-all (the inputs are
+ * the P ranks' [B, S, H/P, D] head-group tensors, the result rank r's sequence shard).  A
+ * sequence-first layout [S, B, H, D] is scatter_dim 2, gather_dim 0; packed QKV [B, S, 3, H, D]
+ * is scatter_dim 3, gather_dim 1.  Bytes are copied verbatim (bit-exact); elem_bytes in
+ * {1, 2, 4, 8}.  out must not overlap any input.
+ * Errors: THA_ERR_INVALID for null pointers, P outside [1, THA_MAX_SHARDS], rank outside
+ * [0, P), ndim outside [1, 8], a size < 1, scatter_dim or gather_dim outside [0, ndim) or equal,
+ * shape[scatter_dim] not divisible by P, or more than 2^48 elements per tensor;
+ * THA_ERR_UNSUPPORTED for other elem_bytes.
+ */
+THA_API int shard_all_to_all(const void* const* inputs, int P, int rank, void* out, int ndim, const long long* shape,
+                             int scatter_dim, int gather_dim, int elem_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 THA_API const char* tha_status_string(int status);
 

@@ -53,8 +53,9 @@ def load_library(path: str = LIB_PATH):
     lib.attn_merge_lse.argtypes = [ci, vp, vp, ci, vp, ci, vp, ci, ci, ci, ci, vp]
     lib.shard_permute.argtypes = [vp, ci, ci, vp, ci, ci, ci, ci, ci, vp]
     lib.shard_unpermute.argtypes = [vp, ci, ci, vp, ci, ci, ci, ci, ci, vp]
+    lib.shard_all_to_all.argtypes = [vp, ci, ci, vp, ci, vp, ci, ci, ci, vp]
     for f in (lib.attn_fwd, lib.attn_fwd_ex, lib.attn_bwd, lib.attn_merge_lse, lib.shard_permute, lib.shard_unpermute,
-              lib.tha_version):
+              lib.shard_all_to_all, lib.tha_version):
         f.restype = ci
     lib.tha_status_string.argtypes = [ci]
     lib.tha_status_string.restype = ctypes.c_char_p
@@ -346,6 +347,40 @@ def shard_unpermute(x: torch.Tensor, group: int, shards: Sequence[torch.Tensor])
     rc = _lib.shard_unpermute(x.data_ptr(), P, int(group), _ptrs(shards), B, S, Hl * P, D, x.element_size(),
                               _stream(x))
     _check(rc, "shard_unpermute")
+
+
+def shard_all_to_all(inputs: Sequence[torch.Tensor], rank: int, scatter_dim: int, gather_dim: int,
+                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """What rank `rank` holds after an all-to-all of the P ranks' tensors `inputs` (one shape and
+    dtype, contiguous): each split into P chunks along scatter_dim, chunk r sent to rank r, the
+    received chunks concatenated in rank order along gather_dim (see tha.h shard_all_to_all).
+    Negative dims count from the end."""
+    load_library()
+    inputs = _shard_list(inputs, "inputs")
+    P = len(inputs)
+    shape = list(inputs[0].shape)
+    nd = len(shape)
+    if not 1 <= nd <= 8:
+        raise ValueError("inputs must have 1 to 8 dims")
+    sd, gd = int(scatter_dim), int(gather_dim)
+    if not (-nd <= sd < nd and -nd <= gd < nd):
+        raise ValueError(f"scatter_dim / gather_dim out of range for {nd} dims")
+    sd, gd = sd % nd, gd % nd
+    if sd == gd:
+        raise ValueError("scatter_dim and gather_dim must differ")
+    if shape[sd] % P:
+        raise ValueError(f"size {shape[sd]} of the scatter dim is not divisible by the rank count {P}")
+    out_shape = list(shape)
+    out_shape[sd] //= P
+    out_shape[gd] *= P
+    if out is None:
+        out = torch.empty(out_shape, dtype=inputs[0].dtype, device=inputs[0].device)
+    _expect(_dev(out, "out"), "out", out_shape, inputs[0].dtype, inputs[0].device)
+    sh = (ctypes.c_longlong * nd)(*shape)
+    rc = _lib.shard_all_to_all(_ptrs(inputs), P, int(rank), out.data_ptr(), nd, sh, sd, gd,
+                               inputs[0].element_size(), _stream(out))
+    _check(rc, "shard_all_to_all")
+    return out
 
 
 class _Attention(torch.autograd.Function):

@@ -204,4 +204,29 @@ int shard_unpermute(const void* in, int P, int group, void* const* shards, int B
   return hip_status(tha::launch_shard_unpermute(in, P, group, sp, B, S, H, D, elem_bytes, (hipStream_t)stream));
 }
 
+int shard_all_to_all(const void* const* inputs, int P, int rank, void* out, int ndim, const long long* shape,
+                     int scatter_dim, int gather_dim, int elem_bytes, void* stream) {
+  if (!inputs || !out || !shape) return THA_ERR_INVALID;
+  if (P < 1 || P > THA_MAX_SHARDS || rank < 0 || rank >= P) return THA_ERR_INVALID;
+  if (ndim < 1 || ndim > 8) return THA_ERR_INVALID;
+  if (scatter_dim < 0 || scatter_dim >= ndim || gather_dim < 0 || gather_dim >= ndim || scatter_dim == gather_dim)
+    return THA_ERR_INVALID;
+  int64_t sh[8], total = 1;
+  for (int d = 0; d < ndim; ++d) {
+    if (shape[d] < 1 || shape[d] > (1LL << 48)) return THA_ERR_INVALID;
+    sh[d] = shape[d];
+    total *= sh[d];
+    if (total > (1LL << 48)) return THA_ERR_INVALID;
+  }
+  if (sh[scatter_dim] % P != 0) return THA_ERR_INVALID;
+  tha::ShardPtrs sp = {};
+  for (int i = 0; i < P; ++i) {
+    if (!inputs[i]) return THA_ERR_INVALID;
+    sp.p[i] = const_cast<void*>(inputs[i]);
+  }
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) return THA_ERR_UNSUPPORTED;
+  return hip_status(
+      tha::launch_all_to_all(sp, P, rank, out, ndim, sh, scatter_dim, gather_dim, elem_bytes, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -59,6 +59,8 @@ hipError_t launch_shard_permute(const ShardPtrs& shards, int P, int group, void*
                                 int elem_bytes, hipStream_t stream);
 hipError_t launch_shard_unpermute(const void* in, int P, int group, const ShardPtrs& shards, int B, int S, int H,
                                   int D, int elem_bytes, hipStream_t stream);
+hipError_t launch_all_to_all(const ShardPtrs& in, int P, int rank, void* out, int ndim, const int64_t* shape,
+                             int scatter_dim, int gather_dim, int elem_bytes, hipStream_t stream);
 hipError_t launch_merge_lse(int n_parts, const PartPtrs& parts, int part_dt, void* o_out, int out_dt, float* lse_out,
                             int B, int S, int H, int D, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);

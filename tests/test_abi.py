@@ -187,3 +187,29 @@ def test_permute_validation(lib):
         assert call(B=0) == E
         assert call(shards=(ctypes.c_void_p * 4)(0x1000, 0x1000, 0, 0x1000)) == E
         assert call(eb=3) == U
+
+
+def test_all_to_all_validation(lib):
+    E, U = T.THA_ERR_INVALID, T.THA_ERR_UNSUPPORTED
+    ins = _ptr_arr(4)
+
+    def call(inputs=ins, Pn=4, rank=0, out=P, shape=(2, 8, 8, 4), sd=2, gd=1, eb=2, nd=None):
+        sh = (ctypes.c_longlong * len(shape))(*shape) if shape is not None else None
+        return lib.shard_all_to_all(inputs, Pn, rank, out, len(shape) if nd is None else nd, sh, sd, gd, eb, None)
+    assert call(inputs=None) == E
+    assert call(out=None) == E
+    assert call(shape=None, nd=4) == E
+    assert call(Pn=0) == E
+    assert call(Pn=65, inputs=_ptr_arr(65)) == E
+    assert call(rank=4) == E
+    assert call(rank=-1) == E
+    assert call(nd=0) == E
+    assert call(shape=(2,) * 9) == E            # more than 8 dims
+    assert call(sd=1, gd=1) == E                # scatter dim == gather dim
+    assert call(sd=4) == E
+    assert call(gd=-1) == E
+    assert call(shape=(2, 8, 6, 4)) == E        # 6 heads over 4 ranks
+    assert call(shape=(2, 0, 8, 4)) == E        # empty dim
+    assert call(shape=(1 << 25, 1 << 25, 8, 1)) == E  # more than 2^48 elements
+    assert call(inputs=(ctypes.c_void_p * 4)(0x1000, 0x1000, 0, 0x1000)) == E
+    assert call(eb=3) == U

@@ -124,3 +124,18 @@ def test_permute_checks(rec):
     T.shard_permute(sh, 1)
     T.shard_unpermute(x, 1, sh)
     assert rec.calls == ["shard_permute", "shard_unpermute"]
+
+
+def test_all_to_all_checks(rec):
+    P = 4
+    ins = [_t(2, 3, 8, 16) for _ in range(P)]
+    _rejects(rec, T.shard_all_to_all, ins[:3] + [_t(2, 3, 8, 8)], 0, 2, 1)        # shapes differ
+    _rejects(rec, T.shard_all_to_all, ins[:3] + [_t(2, 3, 8, 16, dtype=F32)], 0, 2, 1)  # dtypes differ
+    _rejects(rec, T.shard_all_to_all, ins, 0, 1, 1)                                 # same dim twice
+    _rejects(rec, T.shard_all_to_all, ins, 0, 4, 1)                                 # dim out of range
+    _rejects(rec, T.shard_all_to_all, ins, 0, 1, 2)                                 # 3 tokens over 4 ranks
+    _rejects(rec, T.shard_all_to_all, ins, 0, 2, 1, out=_t(2, 3, 2, 16))            # out shape
+    _rejects(rec, T.shard_all_to_all, ins, 0, 2, 1, out=_t(2, 12, 2, 16, dtype=F32))
+    T.shard_all_to_all(ins, 1, 2, 1)
+    T.shard_all_to_all(ins, 1, -2, -3, out=_t(2, 12, 2, 16))
+    assert rec.calls == ["shard_all_to_all", "shard_all_to_all"]
