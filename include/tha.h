@@ -49,7 +49,8 @@ typedef enum {
   THA_OK = 0,
   THA_ERR_INVALID = -1,     /* null pointer, non-positive size, inconsistent sizes */
   THA_ERR_UNSUPPORTED = -2, /* a valid request this build does not implement */
-  THA_ERR_HIP = -3          /* a HIP launch failed */
+  THA_ERR_HIP = -3,         /* a HIP launch failed */
+  THA_ERR_TOO_LARGE = -4    /* exceeds the fixed scratch capacity of a no-allocation entry point */
 } tha_status;
 
 /* Element types. */
@@ -74,6 +75,8 @@ enum {
 /* Largest pointer arrays accepted by attn_merge_lse and the permutes. */
 #define THA_MAX_PARTS 64
 #define THA_MAX_SHARDS 64
+/* Largest B*H*Sq that attn_bwd_noalloc takes (its fixed Delta scratch, 16 MiB per device). */
+#define THA_NOALLOC_MAX_DELTA (4 * 1024 * 1024)
 
 /*
  * attn_fwd -- attention of every query row against the visible keys, per head.
@@ -184,6 +187,22 @@ THA_API int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, in
 THA_API int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
              float* dq, float* dk, float* dv, float* workspace, int B, int Sq, int Sk, int H, int D, int in_dt,
              unsigned mask_flags, long long q_pos0, long long k_pos0, const int* kv_len, float scale, void* stream);
+
+/*
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, results
+ * and errors as attn_bwd without the workspace: Delta lives in a scratch array the library keeps
+ * in device memory, THA_NOALLOC_MAX_DELTA floats (16 MiB) per device for the life of the process.
+ * The call allocates nothing (no hipMalloc / hipFree and no allocating library routine).
+ * B*H*Sq above THA_NOALLOC_MAX_DELTA returns THA_ERR_TOO_LARGE (checked on the host before any HIP
+ * call).  Every call on a device shares that device's scratch array (it is fully rewritten by each
+ * call before it is read), so calls that overlap on one device -- on different streams or from
+ * different host threads without ordering -- race; calls on different devices do not.
+ */
+THA_API int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                             const float* lse, float* dq, float* dk, float* dv, int B, int Sq, int Sk, int H, int D,
+                             int in_dt, unsigned mask_flags, long long q_pos0, long long k_pos0, const int* kv_len,
+                             float scale, void* stream);
 
 /*
  * attn_merge_lse -- combine n partial attention results over disjoint key

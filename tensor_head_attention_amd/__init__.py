@@ -17,12 +17,13 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtha.so")
 
-THA_OK, THA_ERR_INVALID, THA_ERR_UNSUPPORTED, THA_ERR_HIP = 0, -1, -2, -3
+THA_OK, THA_ERR_INVALID, THA_ERR_UNSUPPORTED, THA_ERR_HIP, THA_ERR_TOO_LARGE = 0, -1, -2, -3, -4
 THA_F32, THA_BF16 = 0, 1
 THA_MASK_NONE, THA_MASK_CAUSAL, THA_MASK_KEY_PADDING = 0, 1, 2
 THA_ACCUMULATE = 4
 THA_KERNEL_AUTO, THA_KERNEL_NARROW, THA_KERNEL_WIDE, THA_KERNEL_SPLIT = 0, 1 << 3, 2 << 3, 3 << 3
 THA_MAX_PARTS = THA_MAX_SHARDS = 64
+THA_NOALLOC_MAX_DELTA = 4 * 1024 * 1024
 _KERNELS = {None: THA_KERNEL_AUTO, "auto": THA_KERNEL_AUTO, "narrow": THA_KERNEL_NARROW,
             "wide": THA_KERNEL_WIDE, "split": THA_KERNEL_SPLIT}
 
@@ -50,12 +51,14 @@ def load_library(path: str = LIB_PATH):
                                 ctypes.c_float, vp, vp]
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_uint, cll, cll,
                              vp, ctypes.c_float, vp]
+    lib.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ctypes.c_uint, cll,
+                                     cll, vp, ctypes.c_float, vp]
     lib.attn_merge_lse.argtypes = [ci, vp, vp, ci, vp, ci, vp, ci, ci, ci, ci, vp]
     lib.shard_permute.argtypes = [vp, ci, ci, vp, ci, ci, ci, ci, ci, vp]
     lib.shard_unpermute.argtypes = [vp, ci, ci, vp, ci, ci, ci, ci, ci, vp]
     lib.shard_all_to_all.argtypes = [vp, ci, ci, vp, ci, vp, ci, ci, ci, vp]
-    for f in (lib.attn_fwd, lib.attn_fwd_ex, lib.attn_bwd, lib.attn_merge_lse, lib.shard_permute, lib.shard_unpermute,
-              lib.shard_all_to_all, lib.tha_version):
+    for f in (lib.attn_fwd, lib.attn_fwd_ex, lib.attn_bwd, lib.attn_bwd_noalloc, lib.attn_merge_lse, lib.shard_permute,
+              lib.shard_unpermute, lib.shard_all_to_all, lib.tha_version):
         f.restype = ci
     lib.tha_status_string.argtypes = [ci]
     lib.tha_status_string.restype = ctypes.c_char_p
@@ -78,6 +81,8 @@ def _check(rc: int, what: str):
         raise ValueError(f"{what}: {status_string(rc)}")
     if rc == THA_ERR_UNSUPPORTED:
         raise NotImplementedError(f"{what}: {status_string(rc)}")
+    if rc == THA_ERR_TOO_LARGE:
+        raise ValueError(f"{what}: {status_string(rc)}")
     raise ThaError(rc, what)
 
 
@@ -236,14 +241,7 @@ def attn_fwd_ex(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bo
     return out, lse
 
 
-def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,
-             lse: torch.Tensor, *, causal: bool = False, kv_len: Optional[torch.Tensor] = None, q_pos0: int = 0,
-             k_pos0: int = 0, scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
-             dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
-             workspace: Optional[torch.Tensor] = None):
-    """Gradients of attn_fwd (see tha.h attn_bwd): returns (dq, dk, dv), fp32.  Given dq / dk / dv
-    are accumulated into; missing ones start from zero.  workspace: fp32 of >= B*H*Sq elements."""
-    load_library()
+def _bwd_args(q, k, v, o, dout, lse, kv_len, dq, dk, dv):
     q, k, v, o, dout, lse = (_dev(t, n) for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"),
                                                         (lse, "lse")))
     B, Sq, H, D = _bshd(q, "q")
@@ -262,12 +260,25 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
         dv = torch.zeros((B, Sk, H, D), dtype=torch.float32, device=dev)
     for t, n, S_ in ((dq, "dq", Sq), (dk, "dk", Sk), (dv, "dv", Sk)):
         _expect(_dev(t, n), n, (B, S_, H, D), torch.float32, dev)
-    if workspace is None:
-        workspace = torch.empty((B * H * Sq,), dtype=torch.float32, device=dev)
-    _dev(workspace, "workspace")
-    if workspace.dtype != torch.float32 or workspace.numel() < B * H * Sq or workspace.device != dev:
-        raise ValueError("workspace must be float32 on q's device with at least B*H*Sq elements")
     kflag, kvp = _kv_len_arg(kv_len, B, dev)
+    return (B, Sq, Sk, H, D), (q, k, v, o, dout, lse), (dq, dk, dv), kflag, kvp
+
+
+def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,
+             lse: torch.Tensor, *, causal: bool = False, kv_len: Optional[torch.Tensor] = None, q_pos0: int = 0,
+             k_pos0: int = 0, scale: Optional[float] = None, dq: Optional[torch.Tensor] = None,
+             dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None):
+    """Gradients of attn_fwd (see tha.h attn_bwd): returns (dq, dk, dv), fp32.  Given dq / dk / dv
+    are accumulated into; missing ones start from zero.  workspace: fp32 of >= B*H*Sq elements."""
+    load_library()
+    (B, Sq, Sk, H, D), (q, k, v, o, dout, lse), (dq, dk, dv), kflag, kvp = _bwd_args(q, k, v, o, dout, lse, kv_len,
+                                                                                      dq, dk, dv)
+    if workspace is None:
+        workspace = torch.empty((B * H * Sq,), dtype=torch.float32, device=q.device)
+    _dev(workspace, "workspace")
+    if workspace.dtype != torch.float32 or workspace.numel() < B * H * Sq or workspace.device != q.device:
+        raise ValueError("workspace must be float32 on q's device with at least B*H*Sq elements")
     flags = (THA_MASK_CAUSAL if causal else 0) | kflag
     if scale is None:
         scale = 1.0 / math.sqrt(D)
@@ -275,6 +286,27 @@ def attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(), B, Sq, Sk, H, D,
                        _dt(q.dtype), flags, int(q_pos0), int(k_pos0), kvp, float(scale), _stream(q))
     _check(rc, "attn_bwd")
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, dout: torch.Tensor,
+                     lse: torch.Tensor, *, dq: torch.Tensor, dk: torch.Tensor, dv: torch.Tensor,
+                     causal: bool = False, kv_len: Optional[torch.Tensor] = None, q_pos0: int = 0, k_pos0: int = 0,
+                     scale: Optional[float] = None):
+    """attn_bwd without a workspace (see tha.h attn_bwd_noalloc): the library's fixed per-device
+    scratch holds Delta, so the call allocates nothing; the caller passes the fp32 dq, dk, dv to
+    accumulate into.  B*H*Sq must not exceed THA_NOALLOC_MAX_DELTA.  Overlapping calls on one device
+    race on that scratch."""
+    load_library()
+    (B, Sq, Sk, H, D), (q, k, v, o, dout, lse), (dq, dk, dv), kflag, kvp = _bwd_args(q, k, v, o, dout, lse, kv_len,
+                                                                                      dq, dk, dv)
+    flags = (THA_MASK_CAUSAL if causal else 0) | kflag
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rc = _lib.attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                               lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Sq, Sk, H, D,
+                               _dt(q.dtype), flags, int(q_pos0), int(k_pos0), kvp, float(scale), _stream(q))
+    _check(rc, "attn_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -43,6 +43,49 @@ int check_permute(const void* grouped, const void* const* shards, int P, int gro
 
 }  // namespace
 
+namespace tha {
+
+int attn_bwd_check(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   const float* dq, const float* dk, const float* dv, int B, int Sq, int Sk, int H, int D, int in_dt,
+                   unsigned mask_flags, long long q_pos0, long long k_pos0, const int* kv_len, float scale) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return THA_ERR_INVALID;
+  if (B <= 0 || Sq <= 0 || Sk <= 0 || H <= 0 || D <= 0) return THA_ERR_INVALID;
+  if (mask_flags & ~(unsigned)(THA_MASK_CAUSAL | THA_MASK_KEY_PADDING)) return THA_ERR_INVALID;
+  if ((mask_flags & THA_MASK_KEY_PADDING) && !kv_len) return THA_ERR_INVALID;
+  if (!isfinite(scale) || !(scale > 0.f)) return THA_ERR_INVALID;
+  if (q_pos0 >= kMaxPos || q_pos0 <= -kMaxPos || k_pos0 >= kMaxPos || k_pos0 <= -kMaxPos) return THA_ERR_INVALID;
+  if (!dtype_ok(in_dt)) return THA_ERR_UNSUPPORTED;
+  if ((int64_t)H * D > kMaxRowElems) return THA_ERR_UNSUPPORTED;
+  if (in_dt == THA_BF16 && D != 128 && D != 64) return THA_ERR_UNSUPPORTED;
+  if (in_dt == THA_F32 && D > 256) return THA_ERR_UNSUPPORTED;
+  if (in_dt == THA_BF16) {  // 16-byte loads of q, k, v, dout and 16-byte read-modify-writes of dq, dk, dv
+    const void* p16[7] = {q, k, v, dout, dq, dk, dv};
+    for (const void* p : p16)
+      if ((uintptr_t)p % 16) return THA_ERR_UNSUPPORTED;
+  }
+  return THA_OK;
+}
+
+int attn_bwd_launch(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    float* dq, float* dk, float* dv, float* delta, int B, int Sq, int Sk, int H, int D, int in_dt,
+                    unsigned mask_flags, long long q_pos0, long long k_pos0, const int* kv_len, float scale,
+                    void* stream) {
+  AttnBwdArgs a;
+  a.q = q, a.k = k, a.v = v, a.o = o, a.dout = dout, a.lse = lse;
+  a.dq = dq, a.dk = dk, a.dv = dv, a.delta = delta;
+  a.kv_len = (mask_flags & THA_MASK_KEY_PADDING) ? kv_len : nullptr;
+  a.B = B, a.Sq = Sq, a.Sk = Sk, a.H = H, a.D = D;
+  a.causal = (mask_flags & THA_MASK_CAUSAL) != 0;
+  a.q_pos0 = pos_diff(q_pos0, k_pos0), a.k_pos0 = 0;
+  a.scale = scale;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_attn_bwd_delta(a, in_dt, st);
+  if (e != hipSuccess) return THA_ERR_HIP;
+  return hip_status(in_dt == THA_BF16 ? launch_attn_bwd_bf16(a, st) : launch_attn_bwd_f32(a, st));
+}
+
+}  // namespace tha
+
 extern "C" {
 
 int tha_version(void) { return 100; }
@@ -53,6 +96,7 @@ const char* tha_status_string(int status) {
     case THA_ERR_INVALID: return "invalid argument";
     case THA_ERR_UNSUPPORTED: return "unsupported dtype, head dim or size";
     case THA_ERR_HIP: return "HIP launch failed";
+    case THA_ERR_TOO_LARGE: return "request exceeds the fixed scratch capacity of a no-allocation entry point";
     default: return "unknown status";
   }
 }
@@ -139,33 +183,12 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int out_dt
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse, float* dq,
              float* dk, float* dv, float* workspace, int B, int Sq, int Sk, int H, int D, int in_dt,
              unsigned mask_flags, long long q_pos0, long long k_pos0, const int* kv_len, float scale, void* stream) {
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return THA_ERR_INVALID;
-  if (B <= 0 || Sq <= 0 || Sk <= 0 || H <= 0 || D <= 0) return THA_ERR_INVALID;
-  if (mask_flags & ~(unsigned)(THA_MASK_CAUSAL | THA_MASK_KEY_PADDING)) return THA_ERR_INVALID;
-  if ((mask_flags & THA_MASK_KEY_PADDING) && !kv_len) return THA_ERR_INVALID;
-  if (!isfinite(scale) || !(scale > 0.f)) return THA_ERR_INVALID;
-  if (q_pos0 >= kMaxPos || q_pos0 <= -kMaxPos || k_pos0 >= kMaxPos || k_pos0 <= -kMaxPos) return THA_ERR_INVALID;
-  if (!dtype_ok(in_dt)) return THA_ERR_UNSUPPORTED;
-  if ((int64_t)H * D > kMaxRowElems) return THA_ERR_UNSUPPORTED;
-  if (in_dt == THA_BF16 && D != 128 && D != 64) return THA_ERR_UNSUPPORTED;
-  if (in_dt == THA_F32 && D > 256) return THA_ERR_UNSUPPORTED;
-  if (in_dt == THA_BF16) {  // 16-byte loads of q, k, v, dout and 16-byte read-modify-writes of dq, dk, dv
-    const void* p16[7] = {q, k, v, dout, dq, dk, dv};
-    for (const void* p : p16)
-      if ((uintptr_t)p % 16) return THA_ERR_UNSUPPORTED;
-  }
-  tha::AttnBwdArgs a;
-  a.q = q, a.k = k, a.v = v, a.o = o, a.dout = dout, a.lse = lse;
-  a.dq = dq, a.dk = dk, a.dv = dv, a.delta = workspace;
-  a.kv_len = (mask_flags & THA_MASK_KEY_PADDING) ? kv_len : nullptr;
-  a.B = B, a.Sq = Sq, a.Sk = Sk, a.H = H, a.D = D;
-  a.causal = (mask_flags & THA_MASK_CAUSAL) != 0;
-  a.q_pos0 = pos_diff(q_pos0, k_pos0), a.k_pos0 = 0;
-  a.scale = scale;
-  hipStream_t st = (hipStream_t)stream;
-  hipError_t e = tha::launch_attn_bwd_delta(a, in_dt, st);
-  if (e != hipSuccess) return THA_ERR_HIP;
-  return hip_status(in_dt == THA_BF16 ? tha::launch_attn_bwd_bf16(a, st) : tha::launch_attn_bwd_f32(a, st));
+  if (!workspace) return THA_ERR_INVALID;
+  const int rc = tha::attn_bwd_check(q, k, v, o, dout, lse, dq, dk, dv, B, Sq, Sk, H, D, in_dt, mask_flags, q_pos0,
+                                     k_pos0, kv_len, scale);
+  if (rc != THA_OK) return rc;
+  return tha::attn_bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, Sq, Sk, H, D, in_dt, mask_flags,
+                              q_pos0, k_pos0, kv_len, scale, stream);
 }
 
 int attn_merge_lse(int n_parts, const void* const* o_parts, const float* const* lse_parts, int part_dt, void* o_out,

@@ -55,6 +55,16 @@ struct AttnBwdArgs {
   float scale;
 };
 
+// attn_bwd's argument checks (all but the workspace) and its launch with a given Delta buffer
+// ([B,H,Sq] floats); shared by attn_bwd and attn_bwd_noalloc.
+int attn_bwd_check(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                   const float* dq, const float* dk, const float* dv, int B, int Sq, int Sk, int H, int D, int in_dt,
+                   unsigned mask_flags, long long q_pos0, long long k_pos0, const int* kv_len, float scale);
+int attn_bwd_launch(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    float* dq, float* dk, float* dv, float* delta, int B, int Sq, int Sk, int H, int D, int in_dt,
+                    unsigned mask_flags, long long q_pos0, long long k_pos0, const int* kv_len, float scale,
+                    void* stream);
+
 hipError_t launch_shard_permute(const ShardPtrs& shards, int P, int group, void* out, int B, int S, int H, int D,
                                 int elem_bytes, hipStream_t stream);
 hipError_t launch_shard_unpermute(const void* in, int P, int group, const ShardPtrs& shards, int B, int S, int H,

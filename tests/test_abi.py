@@ -213,3 +213,23 @@ def test_all_to_all_validation(lib):
     assert call(shape=(1 << 25, 1 << 25, 8, 1)) == E  # more than 2^48 elements
     assert call(inputs=(ctypes.c_void_p * 4)(0x1000, 0x1000, 0, 0x1000)) == E
     assert call(eb=3) == U
+
+
+def test_attn_bwd_noalloc_validation(lib):
+    """Every check of attn_bwd, then the scratch capacity, all on the host (no HIP call)."""
+    E, U, L = T.THA_ERR_INVALID, T.THA_ERR_UNSUPPORTED, T.THA_ERR_TOO_LARGE
+
+    def call(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, Sq=8, Sk=8, H=1, D=128, in_dt=1, flags=0,
+             qp=0, kp=0, kv=None, scale=0.088):
+        return lib.attn_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, B, Sq, Sk, H, D, in_dt, flags, qp, kp, kv,
+                                    scale, None)
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
+        assert call(**{name: None}) == E, name
+    assert call(B=0) == E
+    assert call(flags=T.THA_MASK_KEY_PADDING) == E
+    assert call(scale=-1.0) == E
+    assert call(D=96) == U
+    assert call(dq=ctypes.c_void_p(0x1008)) == U
+    assert call(Sq=T.THA_NOALLOC_MAX_DELTA + 1) == L
+    assert call(B=2, H=4, Sq=T.THA_NOALLOC_MAX_DELTA // 8 + 1) == L
+    assert T.status_string(L)
