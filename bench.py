@@ -2,17 +2,19 @@
 """Benchmark: one MI355X's Ulysses share of head/sequence-parallel attention.
 
 A step is one pass of the hot path over one batch of seeded synthetic input:
-three shard_permute calls (Q, K, V: 8 sequence shards [1, 4096, 64, 128] bf16
--> head group 0 over the whole sequence, [1, 32768, 8, 128]) followed by causal
-attn_fwd over S = 32768 for those 8 heads (head_dim 128, bf16 in, fp32
-accumulate, bf16 out + fp32 LSE).  Inputs are resident in HBM before timing.
+the Ulysses layout permute of Q, K and V in one shard_permute_n launch (8
+sequence shards [1, 4096, 64, 128] bf16 each -> head group 0 over the whole
+sequence, [1, 32768, 8, 128]) followed by causal attn_fwd over S = 32768 for
+those 8 heads (head_dim 128, bf16 in, fp32 accumulate, bf16 out + fp32 LSE).
+Inputs are resident in HBM before timing.
 
 value = algorithmic attention FLOP of a step / step time (TFLOP/s), where the
 FLOP count covers only visible (query, key) pairs, 4*D per pair.
 
-Side measurements (not part of `value`): each kernel's own rate, and the Ring
-share (one 4096-row Q chunk at positions 28672.. against 8 KV chunks, fp32
-partials, one 8-way attn_merge_lse).
+Side measurements (not part of `value`, run before the warm-up): each kernel's
+own rate, the backward, the Ring share (one 4096-row Q chunk at positions
+28672.. against 8 KV chunks, fp32 partials, one 8-way attn_merge_lse, and the
+fused form) and the other workloads.
 
 The CPU baseline times the fp64 oracle on a bounded sample of the same
 attention (a set of query rows, all heads) on the host cores.
@@ -122,11 +124,12 @@ def main():
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
+    qkv = ("q", "k", "v")
+
     def step(rec=None):
         if rec is not None:
             rec[0].record()
-        for n in ("q", "k", "v"):
-            T.shard_permute(shards[n], grp, out=grouped[n])
+        T.shard_permute_n([shards[n] for n in qkv], grp, outs=[grouped[n] for n in qkv])  # one launch
         if rec is not None:
             rec[1].record()
         T.attn_fwd(grouped["q"], grouped["k"], grouped["v"], causal=True, out=out, lse=lse)
@@ -155,7 +158,7 @@ def main():
         step(r)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    perm_each = sorted(r[0].elapsed_time(r[1]) / 3.0 for r in recs)   # one permute call
+    perm_each = sorted(r[0].elapsed_time(r[1]) / 3.0 for r in recs)   # per tensor of the Q, K, V launch
     attn_each = sorted(r[1].elapsed_time(r[2]) for r in recs)
     perm_ms = sum(perm_each) / args.steps
     attn_ms = sum(attn_each) / args.steps
@@ -165,7 +168,8 @@ def main():
     attn_tflops = flops / (attn_ms * 1e-3) / 1e12
 
     components = {
-        "shard_permute": {"us_per_call": perm_ms * 1e3, "us_median": perm_each[len(perm_each) // 2] * 1e3,
+        "shard_permute": {"form": "shard_permute_n of Q, K and V in one launch; times per tensor",
+                          "us_per_call": perm_ms * 1e3, "us_median": perm_each[len(perm_each) // 2] * 1e3,
                           "us_min": perm_each[0] * 1e3, "bytes_per_call": permute_bytes,
                           "GB_per_s": permute_bytes / (perm_ms * 1e-3) / 1e9,
                           "frac_hbm_peak": permute_bytes / (perm_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
@@ -179,14 +183,24 @@ def main():
     # before one repeats, far more than the 256 MiB MALL), and write into 8 rotating 64 MiB
     # outputs (512 MiB): neither the reads nor the writes can be served by the MALL
     # (buffers of their own: the step's grouped tensors feed the backward side figure)
+    # (Q, K, V in one launch, each call on the next head group: consecutive calls read distinct
+    # 3 x 64 MiB slices, 8 x 192 MiB before one repeats, into 8 rotating output sets)
     names = ("q", "k", "v")
     pouts = [torch.empty_like(grouped["q"]) for _ in range(8)]
     pb = batch_times(torch, lambda i: T.shard_permute(shards[names[i % 3]], (i // 3) % P, out=pouts[i % 8]))
-    del pouts
-    components["shard_permute_batched"] = {"us_per_call": pb[len(pb) // 2] * 1e3, "us_min": pb[0] * 1e3,
+    components["shard_permute_single_batched"] = {
+        "form": "one tensor per launch", "us_per_call": pb[len(pb) // 2] * 1e3, "us_min": pb[0] * 1e3,
+        "timing": BATCH_NOTE, "GB_per_s": permute_bytes / (pb[len(pb) // 2] * 1e-3) / 1e9,
+        "frac_hbm_peak": permute_bytes / (pb[len(pb) // 2] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    pouts3 = [[torch.empty_like(grouped["q"]) for _ in range(3)] for _ in range(8)]
+    pb3 = batch_times(torch, lambda i: T.shard_permute_n([shards[n] for n in names], i % P, outs=pouts3[i % 8]))
+    del pouts, pouts3
+    per_t = pb3[len(pb3) // 2] / 3.0
+    components["shard_permute_batched"] = {"form": "shard_permute_n of Q, K and V in one launch; times per tensor",
+                                           "us_per_call": per_t * 1e3, "us_min": pb3[0] / 3.0 * 1e3,
                                            "timing": BATCH_NOTE,
-                                           "GB_per_s": permute_bytes / (pb[len(pb) // 2] * 1e-3) / 1e9,
-                                           "frac_hbm_peak": permute_bytes / (pb[len(pb) // 2] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+                                           "GB_per_s": permute_bytes / (per_t * 1e-3) / 1e9,
+                                           "frac_hbm_peak": permute_bytes / (per_t * 1e-3) / 1e9 / PEAK_HBM_GBS}
 
     # plain device copy of 256 MiB: the attainable streaming rate on this machine, and the known size
     # that scales the HBM counters of a profiled run (the first copy)
@@ -220,8 +234,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) rounded to bf16)",
-        "config": {"workload": "ulysses_share_32k: 3x shard_permute of 8 seq-shards [1,4096,64,128] bf16 to "
-                               "head group 0 [1,32768,8,128], then causal attn_fwd S=32768, 8 heads x 128",
+        "config": {"workload": "ulysses_share_32k: shard_permute_n of the 8 seq-shards [1,4096,64,128] bf16 of Q, "
+                               "K and V to head group 0 [1,32768,8,128] (one launch), then causal attn_fwd "
+                               "S=32768, 8 heads x 128",
                    "batch": 1, "seq_len": S, "heads": Hl, "head_dim": D, "shards": P, "group": grp,
                    "parallelism": "one GPU's Ulysses share"},
         "frac_of_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),

@@ -75,6 +75,8 @@ enum {
 /* Largest pointer arrays accepted by attn_merge_lse and the permutes. */
 #define THA_MAX_PARTS 64
 #define THA_MAX_SHARDS 64
+/* Most tensors one shard_permute_n / shard_unpermute_n call moves. */
+#define THA_MAX_PERMUTE_TENSORS 4
 /* Largest B*H*Sq that attn_bwd_noalloc takes (its fixed Delta scratch, 16 MiB per device). */
 #define THA_NOALLOC_MAX_DELTA (4 * 1024 * 1024)
 
@@ -262,6 +264,22 @@ THA_API int shard_permute(const void* const* shards, int P, int group, void* out
  */
 THA_API int shard_unpermute(const void* in, int P, int group, void* const* shards, int B, int S, int H, int D,
                     int elem_bytes, void* stream);
+
+/*
+ * shard_permute_n / shard_unpermute_n -- shard_permute / shard_unpermute of n tensors of the same
+ * shape and element size in one launch (Q, K and V of a Ulysses step: "adv07: Sequence Parallel"
+ * section 5, one all-to-all per tensor), with the tensors' address streams interleaved.  Results
+ * are those of n separate calls, bit for bit.
+ *
+ *   shards  host array of n*P device pointers, tensor-major: shards[t*P + i] is shard i of tensor t
+ *   outs / ins  host array of n device pointers, the grouped tensors [B, S, H/P, D]
+ * 1 <= n <= THA_MAX_PERMUTE_TENSORS; otherwise the arguments, rules and errors of shard_permute
+ * (THA_ERR_INVALID also for n out of range or a null entry in either array).
+ */
+THA_API int shard_permute_n(int n, const void* const* shards, int P, int group, void* const* outs, int B, int S,
+                            int H, int D, int elem_bytes, void* stream);
+THA_API int shard_unpermute_n(int n, const void* const* ins, int P, int group, void* const* shards, int B, int S,
+                              int H, int D, int elem_bytes, void* stream);
 
 /*
  * shard_all_to_all -- the local layout of an all-to-all with a general scatter dim and gather

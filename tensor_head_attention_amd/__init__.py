@@ -23,6 +23,7 @@ THA_MASK_NONE, THA_MASK_CAUSAL, THA_MASK_KEY_PADDING = 0, 1, 2
 THA_ACCUMULATE = 4
 THA_KERNEL_AUTO, THA_KERNEL_NARROW, THA_KERNEL_WIDE, THA_KERNEL_SPLIT = 0, 1 << 3, 2 << 3, 3 << 3
 THA_MAX_PARTS = THA_MAX_SHARDS = 64
+THA_MAX_PERMUTE_TENSORS = 4
 THA_NOALLOC_MAX_DELTA = 4 * 1024 * 1024
 _KERNELS = {None: THA_KERNEL_AUTO, "auto": THA_KERNEL_AUTO, "narrow": THA_KERNEL_NARROW,
             "wide": THA_KERNEL_WIDE, "split": THA_KERNEL_SPLIT}
@@ -57,8 +58,10 @@ def load_library(path: str = LIB_PATH):
     lib.shard_permute.argtypes = [vp, ci, ci, vp, ci, ci, ci, ci, ci, vp]
     lib.shard_unpermute.argtypes = [vp, ci, ci, vp, ci, ci, ci, ci, ci, vp]
     lib.shard_all_to_all.argtypes = [vp, ci, ci, vp, ci, vp, ci, ci, ci, vp]
+    lib.shard_permute_n.argtypes = [ci, vp, ci, ci, vp, ci, ci, ci, ci, ci, vp]
+    lib.shard_unpermute_n.argtypes = [ci, vp, ci, ci, vp, ci, ci, ci, ci, ci, vp]
     for f in (lib.attn_fwd, lib.attn_fwd_ex, lib.attn_bwd, lib.attn_bwd_noalloc, lib.attn_merge_lse, lib.shard_permute,
-              lib.shard_unpermute, lib.shard_all_to_all, lib.tha_version):
+              lib.shard_unpermute, lib.shard_all_to_all, lib.shard_permute_n, lib.shard_unpermute_n, lib.tha_version):
         f.restype = ci
     lib.tha_status_string.argtypes = [ci]
     lib.tha_status_string.restype = ctypes.c_char_p
@@ -381,6 +384,61 @@ def shard_unpermute(x: torch.Tensor, group: int, shards: Sequence[torch.Tensor])
     _check(rc, "shard_unpermute")
 
 
+def shard_permute_n(shard_sets: Sequence[Sequence[torch.Tensor]], group: int,
+                    outs: Optional[Sequence[torch.Tensor]] = None) -> list:
+    """shard_permute of n tensors of one shape (e.g. the Q, K and V shards of a Ulysses step) in one
+    launch: shard_sets[t] are the P sequence shards [B,S/P,H,D] of tensor t.  Returns the n grouped
+    tensors [B,S,H/P,D] (bit-identical to n shard_permute calls)."""
+    load_library()
+    n = len(shard_sets)
+    if not 1 <= n <= THA_MAX_PERMUTE_TENSORS:
+        raise ValueError(f"need 1 to {THA_MAX_PERMUTE_TENSORS} tensors")
+    sets = [_shard_list(ss, f"shard_sets[{t}]") for t, ss in enumerate(shard_sets)]
+    P = len(sets[0])
+    first = sets[0][0]
+    for t, ss in enumerate(sets):
+        if len(ss) != P:
+            raise ValueError("every tensor needs the same number of shards")
+        _expect(ss[0], f"shard_sets[{t}][0]", first.shape, first.dtype, first.device)
+    B, Sl, H, D = _bshd(first, "shard_sets[0][0]")
+    if H % P:
+        raise ValueError(f"heads ({H}) must be divisible by the shard count ({P})")
+    shape = (B, Sl * P, H // P, D)
+    if outs is None:
+        outs = [torch.empty(shape, dtype=first.dtype, device=first.device) for _ in range(n)]
+    if len(outs) != n:
+        raise ValueError("need one output per tensor")
+    for t, o in enumerate(outs):
+        _expect(_dev(o, f"outs[{t}]"), f"outs[{t}]", shape, first.dtype, first.device)
+    rc = _lib.shard_permute_n(n, _ptrs([x for ss in sets for x in ss]), P, int(group), _ptrs(outs), B, Sl * P, H, D,
+                              first.element_size(), _stream(first))
+    _check(rc, "shard_permute_n")
+    return list(outs)
+
+
+def shard_unpermute_n(xs: Sequence[torch.Tensor], group: int, shard_sets: Sequence[Sequence[torch.Tensor]]) -> None:
+    """shard_unpermute of n tensors in one launch: head group `group` of xs[t] [B,S,H/P,D] is written
+    back into the P sequence shards shard_sets[t] [B,S/P,H,D]."""
+    load_library()
+    n = len(xs)
+    if not 1 <= n <= THA_MAX_PERMUTE_TENSORS or len(shard_sets) != n:
+        raise ValueError(f"need 1 to {THA_MAX_PERMUTE_TENSORS} tensors, with one shard set each")
+    xs = [_dev(x, f"xs[{t}]") for t, x in enumerate(xs)]
+    B, S, Hl, D = _bshd(xs[0], "xs[0]")
+    sets = [_shard_list(ss, f"shard_sets[{t}]") for t, ss in enumerate(shard_sets)]
+    P = len(sets[0])
+    if S % P:
+        raise ValueError(f"sequence length ({S}) must be divisible by the shard count ({P})")
+    for t in range(n):
+        _expect(xs[t], f"xs[{t}]", (B, S, Hl, D), xs[0].dtype, xs[0].device)
+        if len(sets[t]) != P:
+            raise ValueError("every tensor needs the same number of shards")
+        _expect(sets[t][0], f"shard_sets[{t}][0]", (B, S // P, Hl * P, D), xs[0].dtype, xs[0].device)
+    rc = _lib.shard_unpermute_n(n, _ptrs(xs), P, int(group), _ptrs([x for ss in sets for x in ss]), B, S, Hl * P, D,
+                                xs[0].element_size(), _stream(xs[0]))
+    _check(rc, "shard_unpermute_n")
+
+
 def shard_all_to_all(inputs: Sequence[torch.Tensor], rank: int, scatter_dim: int, gather_dim: int,
                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """What rank `rank` holds after an all-to-all of the P ranks' tensors `inputs` (one shape and
@@ -449,9 +507,9 @@ def ulysses_share(q_shards: Sequence[torch.Tensor], k_shards: Sequence[torch.Ten
                   kv_len: Optional[torch.Tensor] = None, scale: Optional[float] = None,
                   kernel: Optional[str] = None):
     """One GPU's Ulysses share: the P sequence shards [B,S/P,H,D] of Q, K and V are permuted to head
-    group `group` over the whole sequence (shard_permute) and attended (attn_fwd).
+    group `group` over the whole sequence (one shard_permute_n launch) and attended (attn_fwd).
     Returns (out [B,S,H/P,D], lse [B,H/P,S])."""
-    q, k, v = (shard_permute(s, group) for s in (q_shards, k_shards, v_shards))
+    q, k, v = shard_permute_n([q_shards, k_shards, v_shards], group)
     return attn_fwd(q, k, v, causal=causal, kv_len=kv_len, scale=scale, kernel=kernel)
 
 

@@ -27,15 +27,24 @@ long long pos_diff(long long q_pos0, long long k_pos0) {  // |q_pos0|, |k_pos0| 
 
 bool dtype_ok(int dt) { return dt == THA_F32 || dt == THA_BF16; }
 
-int check_permute(const void* grouped, const void* const* shards, int P, int group, int B, int S, int H, int D,
-                  int elem_bytes) {
+// Checks of the permute calls (n tensors), filling the kernel's pointer block.
+int check_permute_n(int n, const void* const* shards, int P, int group, const void* const* grouped, int B, int S,
+                    int H, int D, int elem_bytes, tha::MultiShardPtrs& mp) {
   if (!grouped || !shards) return THA_ERR_INVALID;
+  if (n < 1 || n > THA_MAX_PERMUTE_TENSORS) return THA_ERR_INVALID;
   if (P < 1 || P > THA_MAX_SHARDS) return THA_ERR_INVALID;
   if (group < 0 || group >= P) return THA_ERR_INVALID;
   if (B <= 0 || S <= 0 || H <= 0 || D <= 0) return THA_ERR_INVALID;
   if (S % P != 0 || H % P != 0) return THA_ERR_INVALID;
-  for (int i = 0; i < P; ++i)
-    if (!shards[i]) return THA_ERR_INVALID;
+  mp = tha::MultiShardPtrs{};
+  for (int t = 0; t < n; ++t) {
+    if (!grouped[t]) return THA_ERR_INVALID;
+    mp.grouped[t] = const_cast<void*>(grouped[t]);
+    for (int i = 0; i < P; ++i) {
+      if (!shards[t * P + i]) return THA_ERR_INVALID;
+      mp.shard[t][i] = const_cast<void*>(shards[t * P + i]);
+    }
+  }
   if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) return THA_ERR_UNSUPPORTED;
   if ((int64_t)H * D > kMaxRowElems) return THA_ERR_UNSUPPORTED;
   return THA_OK;
@@ -211,20 +220,28 @@ int attn_merge_lse(int n_parts, const void* const* o_parts, const float* const* 
 
 int shard_permute(const void* const* shards, int P, int group, void* out, int B, int S, int H, int D, int elem_bytes,
                   void* stream) {
-  const int rc = check_permute(out, shards, P, group, B, S, H, D, elem_bytes);
-  if (rc != THA_OK) return rc;
-  tha::ShardPtrs sp = {};
-  for (int i = 0; i < P; ++i) sp.p[i] = const_cast<void*>(shards[i]);
-  return hip_status(tha::launch_shard_permute(sp, P, group, out, B, S, H, D, elem_bytes, (hipStream_t)stream));
+  return shard_permute_n(1, shards, P, group, &out, B, S, H, D, elem_bytes, stream);
 }
 
 int shard_unpermute(const void* in, int P, int group, void* const* shards, int B, int S, int H, int D, int elem_bytes,
                     void* stream) {
-  const int rc = check_permute(in, (const void* const*)shards, P, group, B, S, H, D, elem_bytes);
+  return shard_unpermute_n(1, &in, P, group, shards, B, S, H, D, elem_bytes, stream);
+}
+
+int shard_permute_n(int n, const void* const* shards, int P, int group, void* const* outs, int B, int S, int H, int D,
+                    int elem_bytes, void* stream) {
+  tha::MultiShardPtrs mp;
+  const int rc = check_permute_n(n, shards, P, group, (const void* const*)outs, B, S, H, D, elem_bytes, mp);
   if (rc != THA_OK) return rc;
-  tha::ShardPtrs sp = {};
-  for (int i = 0; i < P; ++i) sp.p[i] = shards[i];
-  return hip_status(tha::launch_shard_unpermute(in, P, group, sp, B, S, H, D, elem_bytes, (hipStream_t)stream));
+  return hip_status(tha::launch_shard_permute(mp, n, P, group, B, S, H, D, elem_bytes, (hipStream_t)stream));
+}
+
+int shard_unpermute_n(int n, const void* const* ins, int P, int group, void* const* shards, int B, int S, int H, int D,
+                      int elem_bytes, void* stream) {
+  tha::MultiShardPtrs mp;
+  const int rc = check_permute_n(n, (const void* const*)shards, P, group, ins, B, S, H, D, elem_bytes, mp);
+  if (rc != THA_OK) return rc;
+  return hip_status(tha::launch_shard_unpermute(mp, n, P, group, B, S, H, D, elem_bytes, (hipStream_t)stream));
 }
 
 int shard_all_to_all(const void* const* inputs, int P, int rank, void* out, int ndim, const long long* shape,

@@ -12,6 +12,11 @@ namespace tha {
 struct ShardPtrs {
   void* p[THA_MAX_SHARDS];
 };
+// n tensors (at most THA_MAX_PERMUTE_TENSORS) of P shards each, and their grouped tensors.
+struct MultiShardPtrs {
+  void* shard[THA_MAX_PERMUTE_TENSORS][THA_MAX_SHARDS];
+  void* grouped[THA_MAX_PERMUTE_TENSORS];
+};
 struct PartPtrs {
   const void* o[THA_MAX_PARTS];
   const float* lse[THA_MAX_PARTS];
@@ -65,10 +70,10 @@ int attn_bwd_launch(const void* q, const void* k, const void* v, const void* o, 
                     unsigned mask_flags, long long q_pos0, long long k_pos0, const int* kv_len, float scale,
                     void* stream);
 
-hipError_t launch_shard_permute(const ShardPtrs& shards, int P, int group, void* out, int B, int S, int H, int D,
+hipError_t launch_shard_permute(const MultiShardPtrs& ptrs, int n, int P, int group, int B, int S, int H, int D,
                                 int elem_bytes, hipStream_t stream);
-hipError_t launch_shard_unpermute(const void* in, int P, int group, const ShardPtrs& shards, int B, int S, int H,
-                                  int D, int elem_bytes, hipStream_t stream);
+hipError_t launch_shard_unpermute(const MultiShardPtrs& ptrs, int n, int P, int group, int B, int S, int H, int D,
+                                  int elem_bytes, hipStream_t stream);
 hipError_t launch_all_to_all(const ShardPtrs& in, int P, int rank, void* out, int ndim, const int64_t* shape,
                              int scatter_dim, int gather_dim, int elem_bytes, hipStream_t stream);
 hipError_t launch_merge_lse(int n_parts, const PartPtrs& parts, int part_dt, void* o_out, int out_dt, float* lse_out,

@@ -233,3 +233,24 @@ def test_attn_bwd_noalloc_validation(lib):
     assert call(Sq=T.THA_NOALLOC_MAX_DELTA + 1) == L
     assert call(B=2, H=4, Sq=T.THA_NOALLOC_MAX_DELTA // 8 + 1) == L
     assert T.status_string(L)
+
+
+def test_permute_n_validation(lib):
+    E, U = T.THA_ERR_INVALID, T.THA_ERR_UNSUPPORTED
+    for fn in (lib.shard_permute_n, lib.shard_unpermute_n):
+        def call(n=3, Pn=4, sh=None, g=0, outs=None, B=1, S=8, H=8, D=4, eb=2):
+            sh = _ptr_arr(n * Pn) if sh is None else sh
+            outs = _ptr_arr(n) if outs is None else outs
+            if fn is lib.shard_permute_n:
+                return fn(n, sh, Pn, g, outs, B, S, H, D, eb, None)
+            return fn(n, outs, Pn, g, sh, B, S, H, D, eb, None)
+        assert call(n=0, sh=_ptr_arr(4), outs=_ptr_arr(1)) == E
+        assert call(n=5) == E                                       # more than THA_MAX_PERMUTE_TENSORS
+        assert call(outs=(ctypes.c_void_p * 3)(0x1000, 0, 0x1000)) == E
+        bad = _ptr_arr(12)
+        bad[7] = None                                               # tensor 1, shard 3
+        assert call(sh=bad) == E
+        assert call(g=4) == E
+        assert call(S=10) == E
+        assert call(H=6) == E
+        assert call(eb=3) == U

@@ -139,3 +139,19 @@ def test_all_to_all_checks(rec):
     T.shard_all_to_all(ins, 1, 2, 1)
     T.shard_all_to_all(ins, 1, -2, -3, out=_t(2, 12, 2, 16))
     assert rec.calls == ["shard_all_to_all", "shard_all_to_all"]
+
+
+def test_permute_n_checks(rec):
+    P, B, Sl, H, D = 4, 1, 3, 8, 16
+    sets = [[_t(B, Sl, H, D) for _ in range(P)] for _ in range(3)]
+    _rejects(rec, T.shard_permute_n, sets[:2] + [[_t(B, Sl, H, D) for _ in range(P - 1)]], 0)   # shard counts differ
+    _rejects(rec, T.shard_permute_n, sets[:2] + [[_t(B, Sl + 1, H, D) for _ in range(P)]], 0)   # shapes differ
+    _rejects(rec, T.shard_permute_n, sets + [sets[0], sets[1]], 0)                             # five tensors
+    _rejects(rec, T.shard_permute_n, sets, 0, outs=[_t(B, Sl * P, H // P, D)] * 2)              # too few outputs
+    _rejects(rec, T.shard_permute_n, sets, 0, outs=[_t(B, Sl * P, H, D)] * 3)                   # output shape
+    xs = [_t(B, Sl * P, H // P, D) for _ in range(3)]
+    _rejects(rec, T.shard_unpermute_n, xs, 0, sets[:2])                                        # sets != tensors
+    _rejects(rec, T.shard_unpermute_n, xs[:2] + [_t(B, Sl * P, H // P, D, dtype=F32)], 0, sets)
+    T.shard_permute_n(sets, 1)
+    T.shard_unpermute_n(xs, 1, sets)
+    assert rec.calls == ["shard_permute_n", "shard_unpermute_n"]

@@ -54,6 +54,37 @@ def test_permute_and_unpermute_bit_exact(P, B, S, H, D, dtype):
         assert torch.equal(_bits(a.cpu()), _bits(b))
 
 
+@pytest.mark.parametrize("n,P,B,S,H,D,dtype", [
+    (3, 8, 1, 256, 64, 128, torch.bfloat16),   # Q, K, V of a Ulysses step
+    (2, 4, 2, 40, 8, 64, torch.bfloat16),
+    (4, 3, 2, 9, 3, 5, torch.float32),         # element path, the most tensors a call takes
+    (1, 2, 1, 6, 2, 3, torch.bfloat16),
+    (3, 64, 1, 128, 64, 8, torch.bfloat16),    # 64 shards of 2 tokens
+    (2, 16, 2, 64, 32, 16, torch.float32),
+])
+def test_permute_n_equals_separate_calls(n, P, B, S, H, D, dtype):
+    """shard_permute_n / shard_unpermute_n over n tensors in one launch give the bits of n single
+    calls and of the oracle, every head group."""
+    say(f"permute_n n{n} P{P} B{B} S{S} H{H} D{D} {dtype}")
+    g = W.generator(n * 1000 + P * 10 + S)
+    sets = [[W.randn((B, S // P, H, D), g, torch.float32).to(dtype) for _ in range(P)] for _ in range(n)]
+    dsets = [to_dev(*ss) for ss in sets]
+    for grp in sorted({0, P // 2, P - 1}):
+        outs = T.shard_permute_n(dsets, grp)
+        torch.cuda.synchronize()
+        for t in range(n):
+            assert torch.equal(_bits(outs[t].cpu()), _bits(oracle.shard_permute(sets[t], grp))), (grp, t)
+        back = [[torch.zeros_like(x) for x in ss] for ss in dsets]
+        T.shard_unpermute_n(outs, grp, back)
+        ref_back = [[torch.zeros_like(x) for x in ss] for ss in dsets]
+        for t in range(n):
+            T.shard_unpermute(outs[t], grp, ref_back[t])
+        torch.cuda.synchronize()
+        for t in range(n):
+            for a, b in zip(back[t], ref_back[t]):
+                assert torch.equal(_bits(a), _bits(b))
+
+
 def test_permute_unaligned_pointer_uses_element_path():
     P, B, S, H, D = 2, 1, 8, 4, 8
     g = W.generator(5)

@@ -69,12 +69,13 @@ def test_workload2_causal_4k_full():
 
 @pytest.fixture(scope="module")
 def w3():
-    """8 sequence shards of Q, K, V permuted to head group 0 on the device (as bench.py does), and
+    """8 sequence shards of Q, K, V permuted to head group 0 on the device in one shard_permute_n
+    launch (as bench.py does), head group 7 of Q by shard_permute, and
     the causal attention of that group; the host copies are the oracle's own permutes."""
     say("workload 3: 8 shards [4096,64,128] -> [32768,8,128]; causal attention S32768")
     inp, p = W.workload_inputs(3)
     dev = {n: to_dev(*inp[n]) for n in ("q", "k", "v")}
-    grouped = {n: T.shard_permute(dev[n], p["group"]) for n in ("q", "k", "v")}
+    grouped = dict(zip(("q", "k", "v"), T.shard_permute_n([dev[n] for n in ("q", "k", "v")], p["group"])))
     g7 = T.shard_permute(dev["q"], 7)
     out, lse = T.attn_fwd(grouped["q"], grouped["k"], grouped["v"], causal=True)  # the wide kernel, as timed
     torch.cuda.synchronize()
