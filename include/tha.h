@@ -313,7 +313,8 @@ THA_API int shard_all_to_all(const void* const* inputs, int P, int rank, void* o
 /* Static description of a status code (never NULL). */
 THA_API const char* tha_status_string(int status);
 
-/* Library ABI version (major * 100 + minor). */
+/* Library ABI version (major * 100 + minor): 101 adds shard_permute_n, shard_unpermute_n,
+   shard_all_to_all, attn_bwd_noalloc, THA_ERR_TOO_LARGE and the THA_KERNEL_* flags of attn_fwd_ex. */
 THA_API int tha_version(void);
 
 #ifdef __cplusplus

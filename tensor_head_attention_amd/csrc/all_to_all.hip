@@ -127,14 +127,12 @@ hipError_t launch_dir(const ShardPtrs& in, int P, int rank, void* out, int64_t A
   bool aligned = run_bytes % 16 == 0 && (uintptr_t)out % 16 == 0;
   for (int i = 0; i < P && aligned; ++i) aligned = (uintptr_t)in.p[i] % 16 == 0;
   const int64_t total_vecs = total * eb / 16;
-  const int64_t runs = total / R;
-  // the vector path's indices are 32-bit: vectors, runs and every radix below 2^32
+  // the vector path's indices are 32-bit: vectors (hence runs and digits) and every radix below 2^32
   if (aligned && total_vecs < (1LL << 32) && X < (1LL << 32) && M < (1LL << 32)) {
     const FastDiv rv = make_fastdiv((uint32_t)(run_bytes / 16));
     const FastDiv r0 = make_fastdiv((uint32_t)(kG ? M : P));
     const FastDiv r1 = make_fastdiv((uint32_t)(kG ? X : M));
     const FastDiv r2 = make_fastdiv((uint32_t)(kG ? P : X / P));
-    (void)runs;
     const int64_t blocks = (total_vecs + kThreads - 1) / kThreads;
     hipLaunchKernelGGL((a2a_vec_kernel<kG>), dim3((unsigned)blocks), dim3(kThreads), 0, st, in, (char*)out,
                        (uint32_t)total_vecs, rv, r0, r1, r2, (uint32_t)X, (uint32_t)M, (uint32_t)P, (uint32_t)rank,

@@ -27,6 +27,13 @@ long long pos_diff(long long q_pos0, long long k_pos0) {  // |q_pos0|, |k_pos0| 
 
 bool dtype_ok(int dt) { return dt == THA_F32 || dt == THA_BF16; }
 
+// Elements per token of a contiguous [B, S, H, D] tensor, for the default strides; sizes that the
+// checks reject get 1, so forming the strides cannot overflow before they are rejected.
+long long contiguous_row(int H, int D) {
+  const long long hd = (long long)H * D;  // both int: no overflow in 64 bits
+  return (H > 0 && D > 0 && hd <= kMaxRowElems) ? hd : 1;
+}
+
 // Checks of the permute calls (n tensors), filling the kernel's pointer block.
 int check_permute_n(int n, const void* const* shards, int P, int group, const void* const* grouped, int B, int S,
                     int H, int D, int elem_bytes, tha::MultiShardPtrs& mp) {
@@ -97,7 +104,7 @@ int attn_bwd_launch(const void* q, const void* k, const void* v, const void* o, 
 
 extern "C" {
 
-int tha_version(void) { return 100; }
+int tha_version(void) { return 101; }
 
 const char* tha_status_string(int status) {
   switch (status) {
@@ -174,7 +181,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int out_dt, f
              int H, int D, int in_dt, unsigned mask_flags, long long q_pos0, long long k_pos0, const int* kv_len,
              float scale, void* stream) {
   if (mask_flags & (THA_ACCUMULATE | THA_KERNEL_MASK)) return THA_ERR_INVALID;  // attn_fwd_ex only
-  const long long hd = (long long)H * D;
+  const long long hd = contiguous_row(H, D);
   const long long st8[8] = {Sq * hd, hd, Sk * hd, hd, Sk * hd, hd, Sq * hd, hd};
   return fwd_common(q, k, v, o, out_dt, lse, B, Sq, Sk, H, D, in_dt, mask_flags, q_pos0, k_pos0, kv_len, scale, st8,
                     stream);
@@ -183,7 +190,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, int out_dt, f
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, int out_dt, float* lse, int B, int Sq, int Sk,
                 int H, int D, int in_dt, unsigned flags, long long q_pos0, long long k_pos0, const int* kv_len,
                 float scale, const long long* strides, void* stream) {
-  const long long hd = (long long)H * D;
+  const long long hd = contiguous_row(H, D);
   const long long dflt[8] = {Sq * hd, hd, Sk * hd, hd, Sk * hd, hd, Sq * hd, hd};
   return fwd_common(q, k, v, o, out_dt, lse, B, Sq, Sk, H, D, in_dt, flags, q_pos0, k_pos0, kv_len, scale,
                     strides ? strides : dflt, stream);
@@ -251,12 +258,12 @@ int shard_all_to_all(const void* const* inputs, int P, int rank, void* out, int 
   if (ndim < 1 || ndim > 8) return THA_ERR_INVALID;
   if (scatter_dim < 0 || scatter_dim >= ndim || gather_dim < 0 || gather_dim >= ndim || scatter_dim == gather_dim)
     return THA_ERR_INVALID;
+  constexpr int64_t kMaxElems = 1LL << 48;
   int64_t sh[8], total = 1;
   for (int d = 0; d < ndim; ++d) {
-    if (shape[d] < 1 || shape[d] > (1LL << 48)) return THA_ERR_INVALID;
+    if (shape[d] < 1 || shape[d] > kMaxElems / total) return THA_ERR_INVALID;  // total * shape[d] <= 2^48
     sh[d] = shape[d];
     total *= sh[d];
-    if (total > (1LL << 48)) return THA_ERR_INVALID;
   }
   if (sh[scatter_dim] % P != 0) return THA_ERR_INVALID;
   tha::ShardPtrs sp = {};

@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lib):
             "tha_status_string", "tha_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert T.version() >= 100
+    assert T.version() >= 101
 
 
 def test_status_strings(lib):
@@ -82,6 +82,7 @@ def test_attn_fwd_validation(lib):
     assert _attn(lib, D=96) == U                         # bf16 path: D in {64, 128}
     assert _attn(lib, in_dt=0, D=257) == U               # fp32 path: D <= 256
     assert _attn(lib, H=1 << 20, D=128) == U             # token row too long for 32-bit tile offsets
+    assert _attn(lib, H=1 << 30, D=1 << 30, Sq=1 << 30) == U  # H*D*Sq far past 64 bits: rejected, no overflow
 
 
 def _fwdx(lib, q=P, k=P, v=P, o=P, out_dt=1, lse=P, B=2, Sq=8, Sk=8, H=1, D=128, in_dt=1, flags=0, qp=0, kp=0,
@@ -211,6 +212,7 @@ def test_all_to_all_validation(lib):
     assert call(shape=(2, 8, 6, 4)) == E        # 6 heads over 4 ranks
     assert call(shape=(2, 0, 8, 4)) == E        # empty dim
     assert call(shape=(1 << 25, 1 << 25, 8, 1)) == E  # more than 2^48 elements
+    assert call(shape=(1 << 40, 1 << 40, 1 << 40, 4)) == E  # the product would overflow 64 bits
     assert call(inputs=(ctypes.c_void_p * 4)(0x1000, 0x1000, 0, 0x1000)) == E
     assert call(eb=3) == U
 
