@@ -262,7 +262,7 @@ def device_info(torch, dev):
 
 def batch_times(torch, call, batches=5, n=30):
     """Per-call GPU time (ms) of a short kernel: `batches` batches of `n` back-to-back calls, each
-    batch between one pair of events, all queued behind a spin kernel.  Sorted ascending."""
+    batch between one pair of events, all queued behind gpu_busy's burst of work.  Sorted ascending."""
     for i in range(3):
         call(i)
     torch.cuda.synchronize()
@@ -279,11 +279,25 @@ def batch_times(torch, call, batches=5, n=30):
     return sorted(a.elapsed_time(b) / n for a, b in evs)
 
 
-def gpu_busy(torch, ms=30.0):
-    """Queue a spin kernel of about `ms` on the current stream, so the short kernels timed after it
-    are all enqueued before the GPU reaches them: their event intervals then hold GPU time only,
-    not the host's per-call launch overhead."""
-    torch.cuda._sleep(int(ms * 1e-3 * 2.0e9))
+_BUSY = {}
+
+
+def gpu_busy(torch, calls=60):
+    """Queue about 27 ms of attention calls (causal, 16384 tokens x 8 heads x 128, ~0.45 ms each)
+    on the current stream, so the short kernels timed after them are all enqueued before the GPU
+    reaches them: their event intervals then hold GPU time only, not the host's per-call launch
+    overhead.  Real work rather than an idle spin, so the timed kernels start at the clocks the GPU
+    holds under load (after a spin of that length the first milliseconds of kernels ran up to ~20%
+    slower, the clock still rising)."""
+    import tensor_head_attention_amd as T
+    if not _BUSY:
+        g = torch.Generator(device="cuda").manual_seed(7)
+        _BUSY["qkv"] = [torch.randn((1, 16384, 8, 128), generator=g, device="cuda").to(torch.bfloat16)
+                        for _ in range(3)]
+        _BUSY["o"] = torch.empty_like(_BUSY["qkv"][0])
+    q, k, v = _BUSY["qkv"]
+    for _ in range(calls):
+        T.attn_fwd(q, k, v, causal=True, out=_BUSY["o"], return_lse=False)
 
 
 def bwd_side(T, W, torch, dev, grouped, out, lse, S, H, D, fwd_flops, seed):

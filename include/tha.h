@@ -69,6 +69,7 @@ enum {
   THA_KERNEL_NARROW = 1 << 3,
   THA_KERNEL_WIDE = 2 << 3,
   THA_KERNEL_SPLIT = 3 << 3,
+  THA_KERNEL_SPLIT64 = 4 << 3,
   THA_KERNEL_MASK = 7 << 3
 };
 
@@ -108,12 +109,18 @@ enum {
  * or THA_F32 in both cases (fp32 output keeps ring partials unrounded).
  * Kernel choice for bf16, D = 128, by grid size: a wide kernel (256 query rows per
  * workgroup) when its grid holds at least two workgroups per compute unit, else a
- * narrow one (128 rows) when its grid does, else the narrow kernel in split form
+ * narrow one (128 rows) when its grid does, else the narrow kernel in a split form
  * (two wavefront groups per workgroup on the two halves of the key range, merged by
- * log-sum-exp before the output is written).  All three compute the same function;
- * the wide and narrow kernels give identical bits, the split form differs from them
- * only by the association of the two key halves (within the stated tolerances).
- * The automatic choice depends on B*H, Sq and the device's compute-unit count, so the
+ * log-sum-exp before the output is written): on 64-row query tiles (THA_KERNEL_SPLIT64)
+ * when 128-row tiles would leave half the compute units idle, or when the mask is
+ * causal, the 128-row tiles are no more than the compute units and the last of them
+ * needs at least twice the keys of the first (the 64-row tiles, launched heaviest
+ * first, even out the units' loads); else on 128-row tiles (THA_KERNEL_SPLIT).
+ * All four compute the same function; the wide and narrow kernels give identical
+ * bits, the split forms differ from them and from each other only by where the key
+ * range is halved (within the stated tolerances).
+ * The automatic choice depends on B*H, Sq, the causal extent (mask, Sq, Sk and
+ * q_pos0 - k_pos0) and the device's compute-unit count, so the
  * same rows computed by calls of different sizes (a query split, a Ring chunk against
  * the whole call) may differ in the last bits when the calls take different forms;
  * calls that take the same form give the same bits for the same rows.  attn_fwd_ex's

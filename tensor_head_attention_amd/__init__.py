@@ -21,12 +21,12 @@ THA_OK, THA_ERR_INVALID, THA_ERR_UNSUPPORTED, THA_ERR_HIP, THA_ERR_TOO_LARGE = 0
 THA_F32, THA_BF16 = 0, 1
 THA_MASK_NONE, THA_MASK_CAUSAL, THA_MASK_KEY_PADDING = 0, 1, 2
 THA_ACCUMULATE = 4
-THA_KERNEL_AUTO, THA_KERNEL_NARROW, THA_KERNEL_WIDE, THA_KERNEL_SPLIT = 0, 1 << 3, 2 << 3, 3 << 3
+THA_KERNEL_AUTO, THA_KERNEL_NARROW, THA_KERNEL_WIDE, THA_KERNEL_SPLIT, THA_KERNEL_SPLIT64 = 0, 1 << 3, 2 << 3, 3 << 3, 4 << 3
 THA_MAX_PARTS = THA_MAX_SHARDS = 64
 THA_MAX_PERMUTE_TENSORS = 4
 THA_NOALLOC_MAX_DELTA = 4 * 1024 * 1024
 _KERNELS = {None: THA_KERNEL_AUTO, "auto": THA_KERNEL_AUTO, "narrow": THA_KERNEL_NARROW,
-            "wide": THA_KERNEL_WIDE, "split": THA_KERNEL_SPLIT}
+            "wide": THA_KERNEL_WIDE, "split": THA_KERNEL_SPLIT, "split64": THA_KERNEL_SPLIT64}
 
 _lib = None
 
@@ -159,7 +159,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool 
              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
              return_lse: bool = True, kernel: Optional[str] = None):
     """out [B,Sq,H,D], lse [B,H,Sq] (fp32) = attention of q against k/v (see tha.h attn_fwd).
-    kernel: None (automatic) or "narrow" / "wide" / "split" to force the form of the bf16
+    kernel: None (automatic) or "narrow" / "wide" / "split" / "split64" to force the form of the bf16
     head-size-128 kernel (attn_fwd_ex's THA_KERNEL_* flags)."""
     load_library()
     q, k, v = _dev(q, "q"), _dev(k, "k"), _dev(v, "v")

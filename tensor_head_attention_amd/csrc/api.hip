@@ -130,7 +130,7 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, int out_dt,
   if (flags & ~(unsigned)(THA_MASK_CAUSAL | THA_MASK_KEY_PADDING | THA_ACCUMULATE | THA_KERNEL_MASK))
     return THA_ERR_INVALID;
   const unsigned kernel = flags & THA_KERNEL_MASK;
-  if (kernel > THA_KERNEL_SPLIT) return THA_ERR_INVALID;
+  if (kernel > THA_KERNEL_SPLIT64) return THA_ERR_INVALID;
   if ((flags & THA_MASK_KEY_PADDING) && !kv_len) return THA_ERR_INVALID;
   if (!isfinite(scale) || !(scale > 0.f)) return THA_ERR_INVALID;
   if (q_pos0 >= kMaxPos || q_pos0 <= -kMaxPos || k_pos0 >= kMaxPos || k_pos0 <= -kMaxPos) return THA_ERR_INVALID;
@@ -168,6 +168,7 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, int out_dt,
   a.kernel = kernel == THA_KERNEL_NARROW ? tha::AttnArgs::kNarrow
            : kernel == THA_KERNEL_WIDE   ? tha::AttnArgs::kWide
            : kernel == THA_KERNEL_SPLIT  ? tha::AttnArgs::kSplit
+           : kernel == THA_KERNEL_SPLIT64 ? tha::AttnArgs::kSplit64
                                          : tha::AttnArgs::kAuto;
   hipStream_t s = (hipStream_t)stream;
   return hip_status(in_dt == THA_BF16 ? tha::launch_attn_bf16(a, s) : tha::launch_attn_f32(a, s));

@@ -341,15 +341,29 @@ hipError_t launch_d(const AttnArgs& x, hipStream_t st) {
 
 // Head size 128, by grid size (CU count read once per device): the wide kernel (256 rows per
 // workgroup, one workgroup per CU) when its grid fills every CU at least twice; else the narrow
-// one (128 rows, two workgroups per CU) when its grid does; else the narrow kernel in split form
-// (two wavefront groups per workgroup share the key range), so small grids still put two
-// wavefronts on every SIMD.  A caller's forced choice (AttnArgs::kernel) overrides this.
-enum class D128 { kNarrow, kWide, kSplit };
+// one (128 rows, two workgroups per CU) when its grid does; else a split form (two wavefront
+// groups per workgroup share the key range), so small grids still keep every SIMD busy: the
+// 64-row split form when the 128-row one would leave half the CUs idle, or when the call is
+// causal, its 128-row tiles are no more than the CUs (each CU would hold one, and the heaviest
+// sets the time) and its last query tile needs at least twice the keys of its first (then the
+// 64-row tiles, launched heaviest first, even out the CUs' loads); else the 128-row split form
+// (two wavefronts per SIMD; with more tiles than CUs the light ones already fill in behind the
+// heavy ones).  A caller's forced choice (AttnArgs::kernel) overrides this.
+enum class D128 { kNarrow, kWide, kSplit, kSplit64 };
+
+// Keys the causal rows up to row `rows` - 1 see (key padding ignored), clamped to [0, Sk].
+int64_t causal_keys(const AttnArgs& a, int64_t rows) {
+  int64_t d = a.q_pos0 - a.k_pos0;  // |q_pos0|, |k_pos0| < 2^62: no overflow
+  d = d < -(1LL << 40) ? -(1LL << 40) : (d > (1LL << 40) ? (1LL << 40) : d);
+  const int64_t e = d + rows;
+  return e < 0 ? 0 : (e > a.Sk ? a.Sk : e);
+}
 
 D128 choose_d128(const AttnArgs& a) {
   if (a.kernel == AttnArgs::kWide) return D128::kWide;
   if (a.kernel == AttnArgs::kNarrow) return D128::kNarrow;
   if (a.kernel == AttnArgs::kSplit) return D128::kSplit;
+  if (a.kernel == AttnArgs::kSplit64) return D128::kSplit64;
   static std::atomic<int> cu_count[64];  // per device, filled on first use (any thread may fill it)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return D128::kNarrow;
@@ -360,7 +374,11 @@ D128 choose_d128(const AttnArgs& a) {
     cu_count[dev].store(cus, std::memory_order_relaxed);
   }
   if (attn_bf16_d128_wide_blocks(a) >= 2 * (int64_t)cus) return D128::kWide;
-  if (attn_bf16_d128_blocks(a) >= 2 * (int64_t)cus) return D128::kNarrow;
+  const int64_t blocks = attn_bf16_d128_blocks(a);
+  if (blocks >= 2 * (int64_t)cus) return D128::kNarrow;
+  if (2 * blocks <= (int64_t)cus) return D128::kSplit64;
+  if (a.causal && blocks <= (int64_t)cus && 2 * causal_keys(a, a.Sq < 128 ? a.Sq : 128) <= causal_keys(a, a.Sq))
+    return D128::kSplit64;
   return D128::kSplit;
 }
 
@@ -370,7 +388,9 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
   if (a.D == 128) {
     const D128 k = choose_d128(a);
     if (k == D128::kWide) return launch_attn_bf16_d128_wide(a, st);
-    return launch_attn_bf16_d128(a, st, k == D128::kSplit);
+    return launch_attn_bf16_d128(a, st, k == D128::kSplit    ? D128Form::kSplit
+                                        : k == D128::kSplit64 ? D128Form::kSplit64
+                                                              : D128Form::kNarrow);
   }
   if (a.D == 64) return launch_d<64>(a, st);
   return hipErrorInvalidValue;

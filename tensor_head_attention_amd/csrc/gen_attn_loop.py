@@ -277,11 +277,13 @@ def rescale(A):
     A.e("s_nop 1")
 
 
-def dma_groups(which, ahead, buf):
+def dma_groups(which, ahead, buf, nloads=4):
     """Copy of tile t + ahead of K or V into LDS buffer `buf`, without branches: past this group's
     last tile the copy has 0 valid rows (no memory is read; the buffer it fills is not read
     again).  Returned as groups of scalar instructions, each placed after one MFMA of phase A;
-    every SCC producer sits next to its consumer inside a group."""
+    every SCC producer sits next to its consumer inside a group.  nloads: 16-byte copies per lane
+    (4 rows of the tile each) -- 4 when four wavefronts share a tile, 8 when two do (then two
+    copies per group, so the groups of a K and a V copy still fit the 16 phase-A slots)."""
     ptr, rsrc, offs, dst = (S_KP, S_KR, "koff", "kdst") if which == "k" else (S_VP, S_VR, "voff", "vdst")
     g = []
     g.append([f"s_add_u32 {sr(S_TMP)}, {sr(S_T)}, {ahead}",
@@ -297,17 +299,20 @@ def dma_groups(which, ahead, buf):
               f"s_and_b32 {sr(rsrc + 1)}, {sr(ptr + 1)}, 0xffff",
               f"s_mov_b32 {sr(rsrc + 3)}, 0x20000",
               f"s_add_u32 {sr(S_TMP)}, %[{dst}0], {buf * TILE_BYTES}"])
-    for u in range(4):
-        c = [f"s_mov_b32 m0, {sr(S_TMP)}", "s_nop 0", f"buffer_load_dwordx4 %[{offs}{u}], {sr(rsrc, 4)}, 0 offen lds"]
-        if u < 3:
-            c.append(f"s_add_u32 {sr(S_TMP)}, {sr(S_TMP)}, 1024")
+    per_group = nloads // 4
+    for u0 in range(0, nloads, per_group):
+        c = []
+        for u in range(u0, u0 + per_group):
+            c += [f"s_mov_b32 m0, {sr(S_TMP)}", "s_nop 0", f"buffer_load_dwordx4 %[{offs}{u}], {sr(rsrc, 4)}, 0 offen lds"]
+            if u < nloads - 1:
+                c.append(f"s_add_u32 {sr(S_TMP)}, {sr(S_TMP)}, 1024")
         g.append(c)
     g.append([f"s_add_u32 {sr(ptr)}, {sr(ptr)}, %[tstride_lo]",     # advance the running pointer
               f"s_addc_u32 {sr(ptr + 1)}, {sr(ptr + 1)}, %[tstride_hi]"])
     return g
 
 
-def half(A, parity, uid, cold):
+def half(A, parity, uid, cold, nloads=4):
     """Process tile t (= S_T) whose S lives in set A (parity 0) or B (parity 1).  The common path
     (an unmasked tile that moves no running max) runs straight through; the masked block and the
     rescale go to `cold`, emitted after the loop, and branch back."""
@@ -317,7 +322,7 @@ def half(A, parity, uid, cold):
     p = f"{parity}_{uid}"
     # K(t+2) -> K buffer t&1 (held K(t)), V(t+1) -> V buffer (t+1)&1 (held V(t-1)), both consumed
     # before the last barrier; 7 + 7 groups over the 16 phase-A slots
-    extra_a = dma_groups("k", 2, parity) + [[]] + dma_groups("v", 1, 1 - parity)
+    extra_a = dma_groups("k", 2, parity, nloads) + [[]] + dma_groups("v", 1, 1 - parity, nloads)
     A.e(f"s_add_u32 {sr(S_T1)}, {sr(S_T)}, 1")
     A.e(f"s_cmp_lt_u32 {sr(S_T1)}, %[nkt]")
     A.e(f"s_cbranch_scc0 Llast{p}")
@@ -347,7 +352,8 @@ def last(A, parity, uid):
     A.e(f"s_branch Lend_{uid}")
 
 
-def gen_loop():
+def gen_loop(nloads=4):
+    """The loop for tile copies of `nloads` 16-byte copies per lane (see dma_groups)."""
     A = Asm()
     uid = "%="
     # running tile pointers: K starts at tile 2 (tiles 0, 1 are loaded before the loop), V at tile 1
@@ -360,8 +366,8 @@ def gen_loop():
     A.e(f"s_cbranch_scc0 Lend_{uid}")
     A.e(f"Ltop_{uid}:")
     cold = Asm()
-    half(A, 0, uid, cold)
-    half(A, 1, uid, cold)
+    half(A, 0, uid, cold, nloads)
+    half(A, 1, uid, cold, nloads)
     A.e(f"s_cmp_lt_u32 {sr(S_T)}, %[nkt]")
     A.e(f"s_cbranch_scc1 Ltop_{uid}")
     A.e(f"s_branch Lend_{uid}")
@@ -403,14 +409,16 @@ def check_operand_allocation(compiled_asm: str) -> dict:
     no operand lies in a register the loop writes.  Returns {operand: register} of the last
     instance; raises AssertionError on a violation."""
     import re
-    tpl = gen_loop()
+    tpls = {len(t): t for t in (gen_loop(n) for n in LOOP_VARIANTS)}
+    first = next(iter(tpls.values()))[0]
     blocks = re.findall(r";;#ASMSTART\n(.*?);;#ASMEND", compiled_asm, flags=re.S)
-    loops = [b for b in blocks if b.lstrip().startswith(tpl[0].split()[0] + " s80, 0")]
+    loops = [b for b in blocks if b.lstrip().startswith(first.split()[0] + " s80, 0")]
     assert loops, "loop statement not found in the compiled assembly"
     result = {}
     for body in loops:
         got = [l.strip() for l in body.strip().splitlines() if l.strip()]
-        assert len(got) == len(tpl), (len(got), len(tpl))
+        assert len(got) in tpls, (len(got), sorted(tpls))
+        tpl = tpls[len(got)]
         names = {}
         for t, g in zip(tpl, got):
             pat, keys = "", []
@@ -443,17 +451,22 @@ def check_operand_allocation(compiled_asm: str) -> dict:
     return result
 
 
+# Loop variants written to the .inc: copies per lane and tile -> macro name (the first is the one
+# the four-wavefront groups use; the L8 loop serves groups of two wavefronts).
+LOOP_VARIANTS = {4: "THA_ATTN_LOOP_ASM", 8: "THA_ATTN_LOOP_ASM_L8"}
+
+
 def main(out):
-    lines = gen_loop()
     vclob = [f"v{i}" for i in range(V_BASE, V_BASE + 32)] + [f"v{i}" for i in (RS, MX, NEGINF, T0, ALPHA)]
     vclob += [f"v{i}" for i in range(TMP_BASE, TMP_BASE + N_TMP)]
     vclob += [f"v{i}" for i in range(P_BASE, P_BASE + 16)]
     sclob = [f"s{i}" for i in range(80, 100)]
     clob = ", ".join('"%s"' % c for c in vclob + sclob + ["vcc", "scc", "m0", "memory"])
-    body = "".join('      "%s\\n\\t" \\\n' % l for l in lines)
-    txt = ("// Generated by gen_attn_loop.py (do not edit): main loop of the pipelined bf16 attention kernel.\n"
-           "#define THA_ATTN_LOOP_ASM \\\n" + body + "\n"
-           "#define THA_ATTN_LOOP_CLOBBERS " + clob + "\n")
+    txt = "// Generated by gen_attn_loop.py (do not edit): main loop of the pipelined bf16 attention kernel.\n"
+    for nloads, name in LOOP_VARIANTS.items():
+        body = "".join('      "%s\\n\\t" \\\n' % l for l in gen_loop(nloads))
+        txt += f"#define {name} \\\n" + body + "\n"
+    txt += "#define THA_ATTN_LOOP_CLOBBERS " + clob + "\n"
     open(out, "w").write(txt)
 
 

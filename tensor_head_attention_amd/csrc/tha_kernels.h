@@ -39,7 +39,7 @@ struct AttnArgs {
   int64_t q_bs, q_rs, k_bs, k_rs, v_bs, v_rs, o_bs, o_rs;
   bool accumulate;  // o (fp32) and lse hold a running result: merge this call's result into them
   // bf16, head size 128: which form of the kernel runs (kAuto = chosen by grid size)
-  enum Kernel { kAuto, kNarrow, kWide, kSplit } kernel = kAuto;
+  enum Kernel { kAuto, kNarrow, kWide, kSplit, kSplit64 } kernel = kAuto;
 };
 
 struct AttnBwdArgs {
@@ -80,7 +80,9 @@ hipError_t launch_merge_lse(int n_parts, const PartPtrs& parts, int part_dt, voi
                             int B, int S, int H, int D, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t stream);
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t stream);
-hipError_t launch_attn_bf16_d128(const AttnArgs& a, hipStream_t stream, bool split);
+// Forms of the 128-row / 64-row pipelined kernel (attn_bf16_d128.hip).
+enum class D128Form { kNarrow, kSplit, kSplit64 };
+hipError_t launch_attn_bf16_d128(const AttnArgs& a, hipStream_t stream, D128Form form);
 int64_t attn_bf16_d128_blocks(const AttnArgs& a);
 hipError_t launch_attn_bf16_d128_wide(const AttnArgs& a, hipStream_t stream);
 int64_t attn_bf16_d128_wide_blocks(const AttnArgs& a);

@@ -100,7 +100,7 @@ def test_attn_fwd_ex_validation(lib):
     assert _fwdx(lib, flags=T.THA_ACCUMULATE, out_dt=1, strides=ok) == E   # accumulate needs an fp32 o
     assert _fwdx(lib, flags=T.THA_ACCUMULATE, out_dt=0, lse=None, strides=ok) == E  # ... and an lse
     assert _fwdx(lib, flags=64, strides=ok) == E                            # unknown flag bit
-    assert _fwdx(lib, flags=4 << 3, strides=ok) == E                        # unknown kernel form
+    assert _fwdx(lib, flags=5 << 3, strides=ok) == E                        # unknown kernel form
     assert _attn(lib, flags=T.THA_KERNEL_NARROW) == E                      # attn_fwd takes no kernel form
     for kf in (T.THA_KERNEL_NARROW, T.THA_KERNEL_WIDE, T.THA_KERNEL_SPLIT):  # valid forms pass to the next check
         assert _fwdx(lib, flags=kf, q=None, strides=ok) == E

@@ -29,8 +29,9 @@ def test_generated_loop_is_current(tmp_path):
         assert f.read() == out.read_text(), "attn_loop_d128.inc is stale: rerun gen_attn_loop.py"
 
 
-def test_loop_structure():
-    lines = G.gen_loop()
+@pytest.mark.parametrize("nloads", sorted(G.LOOP_VARIANTS))
+def test_loop_structure(nloads):
+    lines = G.gen_loop(nloads)
     # 16 score MFMAs + 16 value MFMAs per tile with a successor, 16 per last tile;
     # two halves x (unmasked, masked) + two last blocks
     n_mfma = sum(l.startswith("v_mfma") for l in lines)
@@ -41,6 +42,24 @@ def test_loop_structure():
             assert 0 <= int(l.split("lgkmcnt(")[1].rstrip(")")) <= 15
     # one barrier per tile (two per unrolled iteration)
     assert sum(l == "s_barrier" for l in lines) == 2
+    # each block with a successor copies one K and one V tile: nloads copies of each, every
+    # copy through its own offset operand, with M0 set (and a wait state) right before it
+    loads = [i for i, l in enumerate(lines) if l.startswith("buffer_load_dwordx4")]
+    assert len(loads) == 4 * 2 * nloads
+    used = {l.split()[1].rstrip(",") for l in lines if l.startswith("buffer_load_dwordx4")}
+    assert used == {f"%[{w}off{u}]" for w in "kv" for u in range(nloads)}
+    for i in loads:
+        assert lines[i - 1] == "s_nop 0" and lines[i - 2].startswith("s_mov_b32 m0, ")
+    # the copies' LDS destinations advance 1 KiB per copy: nloads KiB per wavefront per tile
+    steps = sum(l == "s_add_u32 s84, s84, 1024" for l in lines)
+    assert steps == 4 * 2 * (nloads - 1)
+
+
+def test_l8_loop_differs_from_l4_only_in_the_copies():
+    a, b = G.gen_loop(4), G.gen_loop(8)
+    copy = ("s_mov_b32 m0, ", "s_nop 0", "buffer_load_dwordx4", "s_add_u32 s84, s84, 1024")
+    strip = lambda ls: [l for l in ls if not l.startswith(copy)]  # noqa: E731
+    assert strip(a) == strip(b)
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="hipcc not available")
@@ -51,7 +70,15 @@ def test_operand_registers_do_not_overlap_loop_writes(tmp_path):
            "-o", str(asm), os.path.join(CSRC, "attn_bf16_d128.hip")]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
-    names = G.check_operand_allocation(asm.read_text())
+    text = asm.read_text()
+    names = G.check_operand_allocation(text)
+    # both loop variants were compiled (and so checked): the 4-copy loop of the narrow and split
+    # forms and the 8-copy loop of the 64-row split form, whose extra copy offsets are operands
+    found = {len([l for l in b.strip().splitlines() if l.strip()])
+             for b in re.findall(r";;#ASMSTART\n(.*?);;#ASMEND", text, flags=re.S)}
+    assert {len(G.gen_loop(n)) for n in G.LOOP_VARIANTS} <= found
+    l8_names = set(re.findall(r"%\[(\w+)\]", "\n".join(G.gen_loop(8))))
+    assert {"koff%d" % i for i in range(4, 8)} | {"voff%d" % i for i in range(4, 8)} <= l8_names
     # every named operand of the template was found
     expected = {"ka%d" % i for i in range(8)} | {"va%d" % i for i in range(4)} | \
                {"koff%d" % i for i in range(4)} | {"voff%d" % i for i in range(4)} | \

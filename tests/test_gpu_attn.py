@@ -61,7 +61,7 @@ def _id(c):
 
 # every case on the automatic choice; the bf16 head-size-128 cases also on each kernel forced
 KCASES = [(c, None) for c in CASES] + [(c, kn) for c in CASES if c[4] == 128 and c[5] == torch.bfloat16
-                                       for kn in ("narrow", "wide", "split")]
+                                       for kn in ("narrow", "wide", "split", "split64")]
 
 
 @pytest.mark.parametrize("case,kernel", KCASES, ids=lambda x: _id(x) if isinstance(x, tuple) else str(x))
@@ -125,7 +125,7 @@ def test_attn_kv_len_clamped():
     assert torch.all(out[0] == 0)
 
 
-@pytest.mark.parametrize("kernel", ["narrow", "wide", "split", None])
+@pytest.mark.parametrize("kernel", ["narrow", "wide", "split", "split64", None])
 def test_attn_deterministic_and_q_split(kernel):
     """Repeated calls are bit-identical, and splitting the query rows into chunks
     (each chunk against the full K/V, 'adv07: Sequence Parallel' section 4) gives
@@ -192,3 +192,47 @@ def test_attn_kv_chunks_merged_equal_unchunked():
     assert torch.all(torch.isinf(parts[4][1]))
     check_out(out, ref, torch.bfloat16)
     check_lse(lse, ref_lse, torch.bfloat16)
+
+
+def _expected_form(B, Sq, Sk, H, causal, qp, kp, cus):
+    """The automatic choice for bf16, head size 128 (tha.h attn_fwd), restated."""
+    if B * H * -(-Sq // 256) >= 2 * cus:
+        return "wide"
+    blocks = B * H * -(-Sq // 128)
+    if blocks >= 2 * cus:
+        return "narrow"
+    if 2 * blocks <= cus:
+        return "split64"
+
+    def keys(rows):
+        return min(max(qp - kp + rows, 0), Sk)
+    if causal and blocks <= cus and 2 * keys(min(Sq, 128)) <= keys(Sq):
+        return "split64"
+    return "split"
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 4096, 4096, 8, True, 0, 0),         # causal, as many 128-row tiles as CUs: 64-row split
+    (1, 4096, 4096, 8, True, 28672, 0),     # a Ring chunk wholly in the past: balanced, 128-row split
+    (1, 4096, 4096, 8, False, 0, 0),        # non-causal: 128-row split
+    (1, 1024, 3000, 8, False, 0, 0),        # a quarter of the CUs as 128-row tiles: 64-row split
+    (1, 6144, 6144, 8, True, 0, 0),         # causal, more 128-row tiles than CUs: 128-row split
+    (2, 4096, 4096, 8, True, 0, 0),         # two 128-row tiles per CU: narrow
+    (1, 8192, 8192, 8, True, 0, 0)])        # wide
+def test_attn_automatic_form(shape):
+    """The automatic choice takes the form the rule in tha.h names for the device's CU count: its
+    result equals that form's, forced, bit for bit."""
+    B, Sq, Sk, H, causal, qp, kp = shape
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    form = _expected_form(B, Sq, Sk, H, causal, qp, kp, cus)
+    say(f"automatic form {shape} on {cus} CUs -> {form}")
+    q, k, v, _ = _inputs(B, Sq, Sk, H, 128, torch.bfloat16, seed=Sq + H + B)
+    qd, kd, vd = to_dev(q, k, v)
+    auto = T.attn_fwd(qd, kd, vd, causal=causal, q_pos0=qp, k_pos0=kp)
+    forced = T.attn_fwd(qd, kd, vd, causal=causal, q_pos0=qp, k_pos0=kp, kernel=form)
+    torch.cuda.synchronize()
+    assert torch.equal(auto[0], forced[0]) and torch.equal(auto[1], forced[1])
+    others = [kn for kn in ("narrow", "split", "split64") if kn != form and not (form == "wide" and kn == "narrow")]
+    # the forms differ in the last bits somewhere (so the equality above identifies the form)
+    assert any(not torch.equal(auto[0], T.attn_fwd(qd, kd, vd, causal=causal, q_pos0=qp, k_pos0=kp, kernel=kn)[0])
+               for kn in others)

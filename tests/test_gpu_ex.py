@@ -21,6 +21,7 @@ pytestmark = pytest.mark.gpu
     (2, 300, 3, 128, torch.bfloat16, True, "narrow"),
     (2, 300, 3, 128, torch.bfloat16, True, "wide"),
     (2, 300, 3, 128, torch.bfloat16, True, "split"),
+    (2, 300, 3, 128, torch.bfloat16, True, "split64"),
     (1, 520, 2, 128, torch.bfloat16, False, None),
     (2, 200, 2, 64, torch.bfloat16, True, None),
     (2, 70, 3, 40, torch.float32, True, None),
@@ -41,7 +42,7 @@ def test_packed_qkv_views(B, S, H, D, dt, causal, kernel):
     check_lse(lse, ref_lse, dt)
 
 
-@pytest.mark.parametrize("kernel", ["narrow", "wide", "split"])
+@pytest.mark.parametrize("kernel", ["narrow", "wide", "split", "split64"])
 def test_head_subset_views_and_strided_output(kernel):
     """q, k, v are heads 2..4 of wider [B, S, 8, D] tensors (token stride 8*D), and the output is
     written into heads 1..3 of a [B, S, 6, D] fp32 buffer: the rest of that buffer is untouched."""
@@ -63,7 +64,7 @@ def test_head_subset_views_and_strided_output(kernel):
 
 
 @pytest.mark.parametrize("D,dt,kernel", [(128, torch.bfloat16, "narrow"), (128, torch.bfloat16, "wide"),
-                                         (128, torch.bfloat16, "split"),
+                                         (128, torch.bfloat16, "split"), (128, torch.bfloat16, "split64"),
                                          (64, torch.bfloat16, None), (32, torch.float32, None)])
 def test_fused_ring_step(D, dt, kernel):
     """A late Q chunk against P KV chunks at their global positions (one wholly in the future),

@@ -29,7 +29,7 @@ def big():
     yield dev, ref, ref_lse
 
 
-@pytest.mark.parametrize("kernel", [None, "narrow", "wide", "split"])
+@pytest.mark.parametrize("kernel", [None, "narrow", "wide", "split", "split64"])
 def test_keys_beyond_4GiB(big, kernel):
     (qd, kd, vd, kvd), ref, ref_lse = big
     say(f"large: kernel={kernel}")

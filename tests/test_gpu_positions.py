@@ -17,6 +17,7 @@ BIG = (1 << 62) - 1
 SHIFTS = [-5000, 1 << 40, -(1 << 40), (1 << 61) + 12345, -(1 << 61)]
 # (head dim, dtype, forced head-size-128 kernel)
 KERNELS = [(128, torch.bfloat16, "narrow"), (128, torch.bfloat16, "wide"), (128, torch.bfloat16, "split"),
+           (128, torch.bfloat16, "split64"),
            (64, torch.bfloat16, None), (40, torch.float32, None)]
 
 

@@ -19,6 +19,7 @@ from parity import check_lse, check_out, say, to_dev
 pytestmark = pytest.mark.gpu
 
 KERNELS = [(128, torch.bfloat16, "narrow"), (128, torch.bfloat16, "wide"), (128, torch.bfloat16, "split"),
+           (128, torch.bfloat16, "split64"),
            (64, torch.bfloat16, None), (40, torch.float32, None)]
 
 

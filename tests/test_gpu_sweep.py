@@ -33,7 +33,7 @@ def _cases(seed, n):
 
 
 FWD = [(c, D, kn) for i, c in enumerate(_cases(2024, 24))
-       for D, kn in ([(128, "narrow"), (128, "wide"), (128, "split")] if i % 2 == 0 else [(64, None), (128, None)])]
+       for D, kn in ([(128, "narrow"), (128, "wide"), (128, "split"), (128, "split64")] if i % 2 == 0 else [(64, None), (128, None)])]
 
 
 def _id(x):
@@ -81,7 +81,7 @@ def test_bwd_sweep(case, D):
         check_grad(got, ref, torch.bfloat16, name)
 
 
-@pytest.mark.parametrize("kernel", ["narrow", "wide", "split"])
+@pytest.mark.parametrize("kernel", ["narrow", "wide", "split", "split64"])
 @pytest.mark.parametrize("seed", [5, 6])
 def test_fused_ring_sweep(kernel, seed):
     """Random chunk counts and sizes, a random query position, key padding on some sequences:

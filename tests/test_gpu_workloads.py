@@ -52,14 +52,17 @@ def test_workload1_tiny_fp32_full():
     assert torch.equal(torch.cat(per, dim=2), out)
 
 
-def test_workload2_causal_4k_full():
-    say("workload 2: causal S4096 H8 D128 bf16, whole output")
+@pytest.mark.parametrize("kernel", [None, "split", "narrow"])
+def test_workload2_causal_4k_full(kernel):
+    """The automatic choice (the 64-row split form at this grid, as timed) and the two other forms
+    the grid could take, over the whole output."""
+    say(f"workload 2: causal S4096 H8 D128 bf16, whole output, kernel={kernel}")
     inp, p = W.workload_inputs(2)
     q, k, v = inp["q"], inp["k"], inp["v"]
     assert max(t.abs().max().item() for t in (q, k, v)) < 8  # bf16 output rounding stays < 2e-2
     ref, ref_lse = oracle.attention(q, k, v, causal=True, nthreads=host_threads())
     qd, kd, vd = to_dev(q, k, v)
-    out, lse = T.attn_fwd(qd, kd, vd, causal=True)
+    out, lse = T.attn_fwd(qd, kd, vd, causal=True, kernel=kernel)
     torch.cuda.synchronize()
     check_out(out, ref, torch.bfloat16)
     check_lse(lse, ref_lse, torch.bfloat16)
