@@ -40,6 +40,26 @@ SA_BASE, SB_BASE, Q_BASE, K_BASE, V_BASE = 128, 96, 64, 48, 32
 P_BASE = 160                 # bf16 probabilities of the current tile: P(ks) in v[160 + 4ks : +3]
 O_AGPR = 0                   # O^T accumulators in a[0:63]
 TMP_BASE, N_TMP = 48, 8      # rescale temporaries: the K fragment buffers, idle at that point
+
+
+class Frag:
+    """Fragment prefetch of a loop variant: reads run `pf` fragments ahead of the MFMA that uses
+    them, through pf + 1 rotating 4-register buffers for K at `kbase` and for V at `vbase`."""
+    def __init__(self, pf, kbase, vbase):
+        self.pf, self.kbase, self.vbase = pf, kbase, vbase
+
+    def regs(self):
+        n = 4 * (self.pf + 1)
+        return set(range(self.kbase, self.kbase + n)) | set(range(self.vbase, self.vbase + n))
+
+
+# Two wavefronts per SIMD cover each other's LDS latency: three fragments ahead.  The 64-row split
+# form runs one wavefront per SIMD and has registers to spare (one workgroup per CU): five ahead,
+# its buffers above the pinned sets (v[176:223]).
+FRAG_L4 = Frag(3, K_BASE, V_BASE)
+FRAG_L8 = Frag(5, 176, 200)
+FRAGS = {4: FRAG_L4, 8: FRAG_L8}  # per loop variant (copies per lane)
+FR = FRAG_L4  # the variant being generated
 RS, MX, NEGINF, T0, ALPHA = 31, 30, 29, 28, 27
 # scalar temporaries (clobbered)
 S_T, S_T1, S_KEY, S_ROWS, S_TMP = 80, 81, 82, 83, 84
@@ -103,11 +123,11 @@ def block(A, cur_base, nxt_base, kbuf, vbuf, has_next, mask_next, extra_a=()):
     def issue_k(i):
         kb, tt = divmod(i, 8)
         off = kbuf * TILE_BYTES + kb * 8192
-        k_ops[i] = A.lds(f"ds_read_b128 {vr(K_BASE + 4 * (i % 4), 4)}, %[ka{tt}] offset:{off}")
+        k_ops[i] = A.lds(f"ds_read_b128 {vr(FR.kbase + 4 * (i % (FR.pf + 1)), 4)}, %[ka{tt}] offset:{off}")
 
     def issue_v(i):
         ks, db = divmod(i, 4)
-        base = V_BASE + 4 * (i % 4)
+        base = FR.vbase + 4 * (i % (FR.pf + 1))
         off = vbuf * TILE_BYTES + ks * 4096
         A.lds(f"ds_read_b64_tr_b16 {vr(base, 2)}, %[va{db}] offset:{off}")
         v_ops[i] = A.lds(f"ds_read_b64_tr_b16 {vr(base + 2, 2)}, %[va{db}] offset:{off + 2048}")
@@ -151,17 +171,17 @@ def block(A, cur_base, nxt_base, kbuf, vbuf, has_next, mask_next, extra_a=()):
             slots[min(p + 1, 15)].append(cvt(p))
 
     if has_next:
-        for i in range(3):
+        for i in range(FR.pf):
             issue_k(i)
         for i in range(16):
-            if i + 3 < 16:
-                issue_k(i + 3)
+            if i + FR.pf < 16:
+                issue_k(i + FR.pf)
             else:
-                issue_v(i + 3 - 16)  # the first V fragments of phase B: V(t) is visible since the last barrier
+                issue_v(i + FR.pf - 16)  # the first V fragments of phase B: V(t) is visible since the last barrier
             kb, tt = divmod(i, 8)
             A.wait_for(k_ops[i])
             src2 = "0" if tt == 0 else vr(nxt(kb, 0), 16)
-            A.e(f"v_mfma_f32_32x32x16_bf16 {vr(nxt(kb, 0), 16)}, {vr(K_BASE + 4 * (i % 4), 4)}, "
+            A.e(f"v_mfma_f32_32x32x16_bf16 {vr(nxt(kb, 0), 16)}, {vr(FR.kbase + 4 * (i % (FR.pf + 1)), 4)}, "
                 f"{vr(Q_BASE + 4 * tt, 4)}, {src2}")
             for op in slots[i]:
                 A.e(op)
@@ -171,7 +191,7 @@ def block(A, cur_base, nxt_base, kbuf, vbuf, has_next, mask_next, extra_a=()):
         for i in range(16):
             for op in slots[i]:
                 A.e(op)
-        for i in range(3):
+        for i in range(FR.pf):
             issue_v(i)
 
     bsl = [[] for _ in range(16)]
@@ -222,12 +242,12 @@ def block(A, cur_base, nxt_base, kbuf, vbuf, has_next, mask_next, extra_a=()):
             bsl, _ = pack(stream, bsl, SLOT_BUDGET, nslots=16)
 
     for i in range(16):
-        if i + 3 < 16:
-            issue_v(i + 3)
+        if i + FR.pf < 16:
+            issue_v(i + FR.pf)
         ks, db = divmod(i, 4)
         kb, h = divmod(ks, 2)
         A.wait_for(v_ops[i])
-        A.e(f"v_mfma_f32_32x32x16_bf16 {ar(O_AGPR + 16 * db, 16)}, {vr(V_BASE + 4 * (i % 4), 4)}, "
+        A.e(f"v_mfma_f32_32x32x16_bf16 {ar(O_AGPR + 16 * db, 16)}, {vr(FR.vbase + 4 * (i % (FR.pf + 1)), 4)}, "
             f"{vr(P_BASE + 4 * ks, 4)}, {ar(O_AGPR + 16 * db, 16)}")
         for op in bsl[i]:
             A.e(op)
@@ -353,7 +373,17 @@ def last(A, parity, uid):
 
 
 def gen_loop(nloads=4):
-    """The loop for tile copies of `nloads` 16-byte copies per lane (see dma_groups)."""
+    """The loop for tile copies of `nloads` 16-byte copies per lane (see dma_groups), with that
+    variant's fragment prefetch (FRAGS)."""
+    global FR
+    saved, FR = FR, FRAGS[nloads]
+    try:
+        return _gen_loop(nloads)
+    finally:
+        FR = saved
+
+
+def _gen_loop(nloads):
     A = Asm()
     uid = "%="
     # running tile pointers: K starts at tile 2 (tiles 0, 1 are loaded before the loop), V at tile 1
@@ -409,8 +439,8 @@ def check_operand_allocation(compiled_asm: str) -> dict:
     no operand lies in a register the loop writes.  Returns {operand: register} of the last
     instance; raises AssertionError on a violation."""
     import re
-    tpls = {len(t): t for t in (gen_loop(n) for n in LOOP_VARIANTS)}
-    first = next(iter(tpls.values()))[0]
+    tpls = {len(gen_loop(n)): (gen_loop(n), n) for n in LOOP_VARIANTS}
+    first = next(iter(tpls.values()))[0][0]
     blocks = re.findall(r";;#ASMSTART\n(.*?);;#ASMEND", compiled_asm, flags=re.S)
     loops = [b for b in blocks if b.lstrip().startswith(first.split()[0] + " s80, 0")]
     assert loops, "loop statement not found in the compiled assembly"
@@ -418,7 +448,7 @@ def check_operand_allocation(compiled_asm: str) -> dict:
     for body in loops:
         got = [l.strip() for l in body.strip().splitlines() if l.strip()]
         assert len(got) in tpls, (len(got), sorted(tpls))
-        tpl = tpls[len(got)]
+        tpl, nloads = tpls[len(got)]
         names = {}
         for t, g in zip(tpl, got):
             pat, keys = "", []
@@ -441,7 +471,7 @@ def check_operand_allocation(compiled_asm: str) -> dict:
             if r is None:
                 continue  # literal or special operand
             kind, regs = r
-            written = {"v": WRITTEN_VGPRS, "s": WRITTEN_SGPRS, "a": WRITTEN_AGPRS}[kind]
+            written = {"v": WRITTEN_VGPRS | clobbered_vgprs(nloads), "s": WRITTEN_SGPRS, "a": WRITTEN_AGPRS}[kind]
             assert not (regs & written), f"operand {k} = {v} lies in a register the loop writes"
             for x in regs:
                 other = owner.setdefault((kind, x), k)
@@ -456,17 +486,26 @@ def check_operand_allocation(compiled_asm: str) -> dict:
 LOOP_VARIANTS = {4: "THA_ATTN_LOOP_ASM", 8: "THA_ATTN_LOOP_ASM_L8"}
 
 
+def clobbered_vgprs(nloads):
+    """VGPRs the loop variant writes outside its operands (its clobber list)."""
+    v = set(range(V_BASE, V_BASE + 32)) | {RS, MX, NEGINF, T0, ALPHA}
+    v |= set(range(TMP_BASE, TMP_BASE + N_TMP)) | set(range(P_BASE, P_BASE + 16))
+    return v | FRAGS[nloads].regs()
+
+
 def main(out):
-    vclob = [f"v{i}" for i in range(V_BASE, V_BASE + 32)] + [f"v{i}" for i in (RS, MX, NEGINF, T0, ALPHA)]
-    vclob += [f"v{i}" for i in range(TMP_BASE, TMP_BASE + N_TMP)]
-    vclob += [f"v{i}" for i in range(P_BASE, P_BASE + 16)]
     sclob = [f"s{i}" for i in range(80, 100)]
-    clob = ", ".join('"%s"' % c for c in vclob + sclob + ["vcc", "scc", "m0", "memory"])
     txt = "// Generated by gen_attn_loop.py (do not edit): main loop of the pipelined bf16 attention kernel.\n"
     for nloads, name in LOOP_VARIANTS.items():
         body = "".join('      "%s\\n\\t" \\\n' % l for l in gen_loop(nloads))
         txt += f"#define {name} \\\n" + body + "\n"
-    txt += "#define THA_ATTN_LOOP_CLOBBERS " + clob + "\n"
+    base = [f"v{i}" for i in range(V_BASE, V_BASE + 32)] + [f"v{i}" for i in (RS, MX, NEGINF, T0, ALPHA)]
+    base += [f"v{i}" for i in range(TMP_BASE, TMP_BASE + N_TMP)] + [f"v{i}" for i in range(P_BASE, P_BASE + 16)]
+    for nloads, suffix in ((4, ""), (8, "_L8")):
+        extra = sorted(clobbered_vgprs(nloads) - clobbered_vgprs(4))
+        assert {int(c[1:]) for c in base} | set(extra) == clobbered_vgprs(nloads)
+        clob = ", ".join('"%s"' % c for c in base + [f"v{i}" for i in extra] + sclob + ["vcc", "scc", "m0", "memory"])
+        txt += f"#define THA_ATTN_LOOP_CLOBBERS{suffix} " + clob + "\n"
     open(out, "w").write(txt)
 
 

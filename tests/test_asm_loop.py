@@ -55,11 +55,19 @@ def test_loop_structure(nloads):
     assert steps == 4 * 2 * (nloads - 1)
 
 
-def test_l8_loop_differs_from_l4_only_in_the_copies():
+def test_l8_loop_differs_from_l4_in_copies_and_prefetch_only():
+    """The 8-copy loop makes twice the tile copies and reads fragments five ahead (through its own
+    buffers) instead of three; the arithmetic instructions are the same, in the same order."""
     a, b = G.gen_loop(4), G.gen_loop(8)
-    copy = ("s_mov_b32 m0, ", "s_nop 0", "buffer_load_dwordx4", "s_add_u32 s84, s84, 1024")
-    strip = lambda ls: [l for l in ls if not l.startswith(copy)]  # noqa: E731
-    assert strip(a) == strip(b)
+    keep = ("v_mfma", "v_exp", "v_fma", "v_add", "v_max", "v_cvt", "v_cmp", "v_cndmask", "v_mul", "v_sub",
+            "v_permlane", "v_accvgpr", "s_barrier", "s_cbranch", "s_branch")
+    arith = lambda ls: [re.sub(r"v\[\d+:\d+\]", "F", l) for l in ls if l.startswith(keep)]  # noqa: E731
+    assert arith(a) == arith(b)
+    # every fragment register of the 8-copy loop is one of its six rotating buffers
+    for l in b:
+        if l.startswith("ds_read"):
+            r = int(re.match(r"ds_read_\w+ v\[(\d+):", l).group(1))
+            assert r in G.FRAGS[8].regs()
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC) and shutil.which("hipcc") is None, reason="hipcc not available")
@@ -147,9 +155,18 @@ def _simulate_lds_waits(lines, in_flight):
     return pending
 
 
-@pytest.mark.parametrize("gen", ["narrow", "wide"])
+@pytest.mark.parametrize("gen", ["narrow", "narrow_l8", "wide"])
 def test_lds_waits_cover_every_fragment_use(gen):
-    mod = G if gen == "narrow" else GW
+    mod = GW if gen == "wide" else G
+    saved = G.FR
+    G.FR = G.FRAGS[8] if gen == "narrow_l8" else G.FRAGS[4]  # the 8-copy loop's deeper prefetch
+    try:
+        _check_lds_waits(gen, mod)
+    finally:
+        G.FR = saved
+
+
+def _check_lds_waits(gen, mod):
     for has_next, masked in ((True, False), (True, True), (False, False)):
         for parity in (0, 1):
             A = mod.Asm()
