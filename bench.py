@@ -391,9 +391,9 @@ def ring_side(T, W, torch, dev, seed):
 
 
 def config_side(T, W, torch, dev):
-    """attn_fwd at the two other bf16 workloads: causal S=4096 x 8 heads (one 128-row query tile per
-    workgroup and head: 256 workgroups, the split kernel form), and the padded batch B=4, S=8192,
-    32 heads, non-causal, key lengths drawn per sequence (the wide kernel)."""
+    """attn_fwd at the two other bf16 workloads: causal S=4096 x 8 heads (the automatic choice takes
+    the 64-row split form there: 512 workgroups of 64 query rows, launched heaviest first), and the
+    padded batch B=4, S=8192, 32 heads, non-causal, key lengths drawn per sequence (the wide kernel)."""
     res = {}
     inp, p = W.workload_inputs(2)
     q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))

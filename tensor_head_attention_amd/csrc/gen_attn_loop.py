@@ -16,7 +16,8 @@ Per 64-key tile t, for a wavefront of 32 query rows (the kernel source explains 
   and the fp32 row sums, in pair order, in phase B.  Masked tiles keep the whole softmax and the
   row sums in phase A (the mask adds VALU work to phase B).
   then the lazy running-max update (a branch taken only when some row needs it) and the barrier.
-Fragments are read from LDS three MFMAs ahead (the first V fragments during the last slots of
+Fragments are read from LDS three MFMAs ahead (five in the 8-copy variant, whose single wavefront
+per SIMD has no partner to cover the latency; the first V fragments during the last slots of
 phase A); each wait covers exactly the fragment needed.
 The loop runs over nkt tiles starting at key tile tbase (0, or the second half of the key range
 when two wavefront groups of one workgroup split the keys); tmask counts from tbase.
@@ -26,7 +27,8 @@ Register map (physical VGPRs, pinned by the operand constraints):
   S set A   v[128:159], S set B v[96:127] (scores of the current / next tile, alternating)
   Q^T[t]    v[64+4t : 67+4t]            (bf16 fragments, loaded once)
   P(ks)     v[160+4ks : 163+4ks]        (bf16 probabilities of the current tile, 16 keys per step)
-  K frags   v[48:63], V frags v[32:47]   (rotating prefetch buffers)
+  K frags   v[48:63], V frags v[32:47]   (rotating prefetch buffers; 8-copy variant: six each,
+                                          v[176:199] and v[200:223])
   v31 row sum, v30 row max, v29 -inf, v28/v27 temporaries (the rescale also uses v[48:55]); s[80:99] scalar
   temporaries.
 Wait states: every VALU read of an MFMA result, and every MFMA read of a VALU result, is separated
