@@ -155,3 +155,32 @@ def test_permute_n_checks(rec):
     T.shard_permute_n(sets, 1)
     T.shard_unpermute_n(xs, 1, sets)
     assert rec.calls == ["shard_permute_n", "shard_unpermute_n"]
+
+
+def test_kernel_names_map_to_flag_bits(monkeypatch):
+    """kernel= reaches attn_fwd_ex as the THA_KERNEL_* bits of its flags (argument 12), next to the
+    mask bits; no name means the automatic choice through attn_fwd."""
+    seen = []
+
+    class _Args:
+        def __getattr__(self, name):
+            def fn(*args):
+                seen.append((name, args))
+                return 0
+            return fn
+    monkeypatch.setattr(T, "_lib", _Args())
+    monkeypatch.setattr(T, "_is_device", lambda t: True)
+    monkeypatch.setattr(T, "_stream", lambda t: 0)
+    q = _t(1, 8, 2, 128)
+    names = {"narrow": T.THA_KERNEL_NARROW, "wide": T.THA_KERNEL_WIDE, "split": T.THA_KERNEL_SPLIT,
+             "split64": T.THA_KERNEL_SPLIT64}
+    assert len(set(names.values()) | {T.THA_KERNEL_AUTO}) == 5
+    for name, bits in names.items():
+        seen.clear()
+        T.attn_fwd(q, q, q, causal=True, kernel=name)
+        assert [n for n, _ in seen] == ["attn_fwd_ex"]
+        assert seen[0][1][12] == T.THA_MASK_CAUSAL | bits, name
+    for name in (None, "auto"):
+        seen.clear()
+        T.attn_fwd(q, q, q, causal=True, kernel=name)
+        assert [n for n, _ in seen] == ["attn_fwd"] and seen[0][1][12] == T.THA_MASK_CAUSAL
