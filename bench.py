@@ -222,7 +222,7 @@ def main():
         cpu = cpu_baseline(grouped, S, Hl, D, args.cpu_rows)
 
     line = {
-        "metric": "attention fwd TFLOP/s (bf16, causal S=32k, 8x128 heads); % of MFMA peak",
+        "metric": "attention fwd TFLOP/s (bf16, causal S=32k, 8×128 heads); % of MFMA peak",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
